@@ -1,0 +1,183 @@
+/*
+ * libpld: batched prompt-lookup (n-gram) drafting on AMD Instinct MI355X.
+ *
+ * The operation (HyperQwen lookup-drafting page, "lookup drafting: the
+ * three-step principle", step 1): for every request of a batch, find the
+ * longest suffix of its own int32 token history, between n_min and n_max
+ * tokens, that occurred earlier in that history (the earlier occurrence may
+ * overlap the suffix); among occurrences of that length take the most recent;
+ * the tokens that followed it, at most k_max of them (the verify-block bound
+ * of step 2 on the same page, and of section 4 of the Strata prompt-lookup
+ * page), are the draft.
+ *
+ * Exactly, for a history h[0..L) (this is the contract the kernels meet):
+ *   S = { (m, j) : n_min <= m <= n_max, 0 <= j, j + m <= L - 1,
+ *                  h[j .. j+m) == h[L-m .. L) }
+ *   S empty     -> draft_len = 0, match_len = 0, start = -1, row all -1
+ *   otherwise   -> (m, j) = maximum of S by m first, then j;
+ *                  d = min(k_max, L - (j + m));
+ *                  row[0..d) = h[j+m .. j+m+d), row[d..k_max) = -1;
+ *                  draft_len = d, match_len = m, start = j.
+ * The suffix never matches itself (j = L - m is excluded) and an occurrence
+ * is always followed by at least one token. Tokens are compared as raw 32-bit
+ * integers. Matches longer than n_max are reported as n_max.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named "device" are HIP device memory of the device that was
+ *    current when the context was created; call with that device current.
+ *  - Calls taking a stream enqueue work on it and return without waiting;
+ *    results are ready when the stream's work up to that point is done.
+ *    Caller buffers must stay valid until then.
+ *  - Host-side argument checks run before anything is enqueued; a failed
+ *    check returns PLD_EINVAL and enqueues nothing. pld_last_error() then
+ *    names the argument.
+ *  - Problems only visible on the device (a bad per-request length or row
+ *    pointer, an append past capacity) do not stop the call: the affected
+ *    request is written as "no match" (or its append is dropped) and a sticky
+ *    flag is set, which pld_sync() reports and clears.
+ *  - Only pld_create allocates. No other entry point allocates memory.
+ *  - A context must not be used from two host threads at once, and two
+ *    draft or append calls on one context must not overlap in time on the
+ *    device (they share the context's per-request reduction slots): issue them
+ *    on one stream, or order the streams.
+ */
+#ifndef PLD_H_
+#define PLD_H_
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pld_ctx pld_ctx; /* opaque; owned by the library */
+
+typedef enum pld_status {
+    PLD_OK = 0,
+    PLD_EINVAL = 1,    /* bad argument, or bad per-request input seen on device */
+    PLD_ENOMEM = 2,    /* device allocation failed in pld_create */
+    PLD_EHIP = 3,      /* a HIP runtime call or kernel launch failed */
+    PLD_ECAPACITY = 4  /* a history longer than max_len, or an append past it */
+} pld_status;
+
+/* Largest n_max accepted (the kernels keep n_max - 1 tokens of left context
+   per tile). The page's own setting is n_max = 12. */
+#define PLD_N_MAX_LIMIT 64
+
+/*
+ * Create a context for batches of up to max_batch requests whose histories
+ * are at most max_len tokens (1 <= max_len <= 2^31 - 1).
+ *
+ * The context holds 16 bytes of reduction state per request, a sticky error
+ * word and, when own_store != 0, a history store of max_batch rows of
+ * max_len tokens (row pitch rounded up to 64 tokens) with a length per row,
+ * all lengths starting at 0 (fed by pld_append; the Strata prompt-lookup page,
+ * section 4, keeps its history index growing by O(1) appends).
+ *
+ * out: receives the context (unchanged on failure).
+ * Errors: PLD_EINVAL (bad sizes, null out), PLD_ENOMEM, PLD_EHIP.
+ * Synchronous: returns once the context's memory is allocated and cleared.
+ */
+pld_status pld_create(pld_ctx **out, int32_t max_batch, int32_t max_len,
+                      int32_t own_store);
+
+/* Free everything the context owns. Waits for the device to finish work
+   first. NULL is a no-op. */
+pld_status pld_destroy(pld_ctx *ctx);
+
+/*
+ * Tuning controls. They never change results, only how the scan is split:
+ *  tile_tokens: candidate positions per workgroup, one of 256, 1024, 2048,
+ *               4096 (default), 8192; 0 keeps the current value.
+ *  fused_gather: 1 (default) lets the last workgroup of each request emit
+ *               its draft inside the scan kernel; 0 emits drafts with a
+ *               second kernel; -1 keeps the current value.
+ * Errors: PLD_EINVAL for other values.
+ */
+pld_status pld_configure(pld_ctx *ctx, int32_t tile_tokens, int32_t fused_gather);
+
+/*
+ * Streaming append into the context's own store (own_store != 0).
+ *
+ * For b < batch: tokens[b * tokens_stride + t] for t < counts[b] are appended
+ * to row b, whose length grows by counts[b].
+ *  tokens: device int32, row b at tokens + b * tokens_stride;
+ *          tokens_stride >= 0 tokens.
+ *  counts: device int32[batch], each 0 <= counts[b].
+ * A row whose append would pass max_len, or whose count is negative, is left
+ * unchanged and sets the sticky flag (PLD_ECAPACITY / PLD_EINVAL at
+ * pld_sync). batch == 0 is a no-op.
+ * Errors: PLD_EINVAL (no store, batch outside [0, max_batch], null pointers,
+ * negative stride), PLD_EHIP.
+ */
+pld_status pld_append(pld_ctx *ctx, const int32_t *tokens, int64_t tokens_stride,
+                      const int32_t *counts, int32_t batch, hipStream_t stream);
+
+/*
+ * Device views of the context's store, for pld_draft_batch:
+ *  *histories: device array of max_batch row pointers;
+ *  *lengths:   device int32[max_batch] current row lengths.
+ * Both stay owned by the context. Errors: PLD_EINVAL (no store, null out).
+ */
+pld_status pld_store_views(pld_ctx *ctx, const int32_t *const **histories,
+                           const int32_t **lengths);
+
+/* Set every store row's length to 0 (stream-ordered). Errors: PLD_EINVAL
+   (no store), PLD_EHIP. */
+pld_status pld_store_reset(pld_ctx *ctx, hipStream_t stream);
+
+/*
+ * Draft every request of a batch (the operation stated at the top).
+ *
+ *  histories: device array of batch row pointers; row b holds lengths[b]
+ *             int32 tokens, 4-byte aligned (any offset; 16-byte alignment is
+ *             fastest). Rows may alias each other and the store.
+ *  lengths:   device int32[batch], 0 <= lengths[b] <= max_len.
+ *  batch:     0 <= batch <= max_batch; 0 is a no-op.
+ *  n_min, n_max: 1 <= n_min <= n_max <= PLD_N_MAX_LIMIT.
+ *  k_max:     >= 1.
+ *  out_draft: device int32[batch * k_max], row-major, row b at b * k_max.
+ *  out_len:   device int32[batch], draft lengths.
+ *  out_match: device int32[batch], match lengths (0 = no match).
+ * A request whose length is outside [0, max_len], or whose row pointer is
+ * null (with a nonzero length) or not 4-byte aligned, is written as no match
+ * and sets the sticky flag.
+ * Errors: PLD_EINVAL, PLD_EHIP.
+ */
+pld_status pld_draft_batch(pld_ctx *ctx, const int32_t *const *histories,
+                           const int32_t *lengths, int32_t batch, int32_t n_min,
+                           int32_t n_max, int32_t k_max, int32_t *out_draft,
+                           int32_t *out_len, int32_t *out_match,
+                           hipStream_t stream);
+
+/* pld_draft_batch plus out_pos: device int32[batch], the occurrence start j
+   (-1 when no match). */
+pld_status pld_draft_batch_pos(pld_ctx *ctx, const int32_t *const *histories,
+                               const int32_t *lengths, int32_t batch,
+                               int32_t n_min, int32_t n_max, int32_t k_max,
+                               int32_t *out_draft, int32_t *out_len,
+                               int32_t *out_match, int32_t *out_pos,
+                               hipStream_t stream);
+
+/*
+ * Wait for the stream, then report and clear the sticky device-side flag:
+ * PLD_OK when clear; PLD_ECAPACITY when a history exceeded max_len or an
+ * append overflowed; PLD_EINVAL when a length or count was negative or a
+ * row pointer was null or misaligned (capacity wins when both are set).
+ * Errors: PLD_EINVAL (null ctx), PLD_EHIP.
+ */
+pld_status pld_sync(pld_ctx *ctx, hipStream_t stream);
+
+/* Static description of a status code. Never NULL. */
+const char *pld_strerror(pld_status status);
+
+/* Details of the last failed call on this host thread ("" if none). */
+const char *pld_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PLD_H_ */

@@ -6,14 +6,12 @@ ctypes layer over it with the same entry-point names. ``workloads`` holds the
 seeded synthetic inputs. PyTorch is used only for device memory and streams.
 """
 
+import importlib
+
 __all__ = ["binding", "workloads"]
 
 
 def __getattr__(name):
-    if name == "binding":
-        from . import binding
-        return binding
-    if name == "workloads":
-        from . import workloads
-        return workloads
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

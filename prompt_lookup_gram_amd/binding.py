@@ -1,0 +1,249 @@
+"""ctypes binding for libpld (include/pld.h), with the same entry-point names.
+
+Argument marshalling only: every step of the drafting path runs in the HIP
+kernels of ``libpld.so``. Tensors must be int32, contiguous and on the GPU;
+raw device pointers (Python ints) are accepted too. The stream defaults to
+PyTorch's current stream. If ``libpld.so`` cannot be loaded the calls raise:
+there is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpld.so")
+
+PLD_OK = 0
+PLD_EINVAL = 1
+PLD_ENOMEM = 2
+PLD_EHIP = 3
+PLD_ECAPACITY = 4
+PLD_N_MAX_LIMIT = 64
+
+# every symbol include/pld.h declares
+EXPORTS = ("pld_create", "pld_destroy", "pld_configure", "pld_append",
+           "pld_store_views", "pld_store_reset", "pld_draft_batch",
+           "pld_draft_batch_pos", "pld_sync", "pld_strerror", "pld_last_error")
+
+_lib = None
+
+
+class PldError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{fn}: {pld_strerror(status)} ({status}): {detail}")
+
+
+def load(path: str = LIB_PATH):
+    """Load libpld.so (building it in-tree first if it was never built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    sig = {
+        "pld_create": [ctypes.POINTER(vp), i32, i32, i32],
+        "pld_destroy": [vp],
+        "pld_configure": [vp, i32, i32],
+        "pld_append": [vp, vp, i64, vp, i32, vp],
+        "pld_store_views": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp)],
+        "pld_store_reset": [vp, vp],
+        "pld_draft_batch": [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp],
+        "pld_draft_batch_pos": [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp],
+        "pld_sync": [vp, vp],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.pld_strerror.argtypes = [ctypes.c_int]
+    lib.pld_strerror.restype = ctypes.c_char_p
+    lib.pld_last_error.argtypes = []
+    lib.pld_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev_ptr(x, name: str, dtype=None) -> int:
+    """Device pointer of a GPU tensor (checked), or a raw pointer int."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor or a device pointer")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name}: tensor must be on the GPU (got {x.device})")
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: tensor must be contiguous")
+    if dtype is not None and x.dtype != dtype:
+        raise ValueError(f"{name}: dtype must be {dtype} (got {x.dtype})")
+    return x.data_ptr()
+
+
+def _check(fn: str, status: int):
+    if status != PLD_OK:
+        raise PldError(fn, status, pld_last_error())
+
+
+def _i32():
+    import torch
+    return torch.int32
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+
+def pld_strerror(status: int) -> str:
+    return load().pld_strerror(int(status)).decode()
+
+
+def pld_last_error() -> str:
+    return load().pld_last_error().decode()
+
+
+def pld_create(max_batch: int, max_len: int, own_store: bool = False) -> int:
+    ctx = ctypes.c_void_p()
+    _check("pld_create", load().pld_create(ctypes.byref(ctx), int(max_batch),
+                                           int(max_len), int(bool(own_store))))
+    return ctx.value
+
+
+def pld_destroy(ctx: int) -> None:
+    _check("pld_destroy", load().pld_destroy(ctx))
+
+
+def pld_configure(ctx: int, tile_tokens: int = 0, fused_gather: int = -1) -> None:
+    _check("pld_configure", load().pld_configure(ctx, int(tile_tokens),
+                                                 int(fused_gather)))
+
+
+def pld_append(ctx: int, tokens, tokens_stride: int, counts, batch: int,
+               stream=None) -> None:
+    i32 = _i32()
+    _check("pld_append", load().pld_append(
+        ctx, _dev_ptr(tokens, "tokens", i32), int(tokens_stride),
+        _dev_ptr(counts, "counts", i32), int(batch), _stream(stream)))
+
+
+def pld_store_views(ctx: int):
+    """(histories, lengths) device pointers of the context's store."""
+    h, n = ctypes.c_void_p(), ctypes.c_void_p()
+    _check("pld_store_views", load().pld_store_views(ctx, ctypes.byref(h),
+                                                     ctypes.byref(n)))
+    return h.value, n.value
+
+
+def pld_store_reset(ctx: int, stream=None) -> None:
+    _check("pld_store_reset", load().pld_store_reset(ctx, _stream(stream)))
+
+
+def pld_draft_batch(ctx: int, histories, lengths, batch: int, n_min: int,
+                    n_max: int, k_max: int, out_draft, out_len, out_match,
+                    stream=None) -> None:
+    import torch
+    i32 = _i32()
+    _check("pld_draft_batch", load().pld_draft_batch(
+        ctx, _dev_ptr(histories, "histories", torch.int64),
+        _dev_ptr(lengths, "lengths", i32), int(batch), int(n_min), int(n_max),
+        int(k_max), _dev_ptr(out_draft, "out_draft", i32),
+        _dev_ptr(out_len, "out_len", i32), _dev_ptr(out_match, "out_match", i32),
+        _stream(stream)))
+
+
+def pld_draft_batch_pos(ctx: int, histories, lengths, batch: int, n_min: int,
+                        n_max: int, k_max: int, out_draft, out_len, out_match,
+                        out_pos, stream=None) -> None:
+    import torch
+    i32 = _i32()
+    _check("pld_draft_batch_pos", load().pld_draft_batch_pos(
+        ctx, _dev_ptr(histories, "histories", torch.int64),
+        _dev_ptr(lengths, "lengths", i32), int(batch), int(n_min), int(n_max),
+        int(k_max), _dev_ptr(out_draft, "out_draft", i32),
+        _dev_ptr(out_len, "out_len", i32), _dev_ptr(out_match, "out_match", i32),
+        _dev_ptr(out_pos, "out_pos", i32), _stream(stream)))
+
+
+def pld_sync(ctx: int, stream=None) -> int:
+    """Wait for the stream; return (and clear) the sticky device status."""
+    return int(load().pld_sync(ctx, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# device-memory plumbing for callers holding numpy histories
+# ---------------------------------------------------------------------------
+
+
+class DeviceBatch:
+    """Histories packed into one device buffer, with a row-pointer table and
+    a lengths vector, ready for pld_draft_batch.
+
+    Row b starts at a multiple of `align` tokens plus `offsets[b]` tokens
+    (offsets let tests place rows at every 4-byte alignment).
+    """
+
+    def __init__(self, histories, device="cuda", align: int = 64,
+                 offsets=None, max_len: int | None = None):
+        import torch
+        self.batch = len(histories)
+        lens = np.array([len(h) for h in histories], dtype=np.int64)
+        offs = np.zeros(self.batch, np.int64) if offsets is None else np.asarray(offsets, np.int64)
+        starts = np.zeros(self.batch, dtype=np.int64)
+        pos = 0
+        for b in range(self.batch):
+            pos = -(-pos // align) * align + int(offs[b])
+            starts[b] = pos
+            pos += int(lens[b])
+        total = -(-pos // align) * align + align
+        flat = np.zeros(total, dtype=np.int32)
+        for b, h in enumerate(histories):
+            flat[starts[b]:starts[b] + lens[b]] = h
+        self.flat = torch.from_numpy(flat).to(device)
+        base = self.flat.data_ptr()
+        self.rows = torch.from_numpy((base + 4 * starts).astype(np.int64)).to(device)
+        self.lengths = torch.from_numpy(lens.astype(np.int32)).to(device)
+        self.starts = starts
+        self.max_len = int(max_len if max_len is not None else max(1, lens.max(initial=1)))
+
+    def replicate(self):
+        """A second copy at another address (same layout)."""
+        other = object.__new__(DeviceBatch)
+        other.batch = self.batch
+        other.flat = self.flat.clone()
+        other.rows = (self.rows - self.flat.data_ptr() + other.flat.data_ptr()).clone()
+        other.lengths = self.lengths
+        other.starts = self.starts
+        other.max_len = self.max_len
+        return other
+
+
+def alloc_outputs(batch: int, k_max: int, device="cuda"):
+    import torch
+    return (torch.empty((batch, k_max), dtype=torch.int32, device=device),
+            torch.empty(batch, dtype=torch.int32, device=device),
+            torch.empty(batch, dtype=torch.int32, device=device),
+            torch.empty(batch, dtype=torch.int32, device=device))

@@ -1,0 +1,349 @@
+// C-ABI entry points of libpld (declared in include/pld.h): argument checks,
+// the context (reduction slots, error word, optional history store) and the
+// launch of the HIP kernels in pld_kernels.hip. No compute happens here.
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include <hip/hip_runtime_api.h>
+
+#include "pld.h"
+#include "pld_kernels.h"
+
+struct pld_ctx {
+    int device;
+    int32_t max_batch;
+    int32_t max_len;
+    int32_t tile_tokens;
+    int32_t fused;
+    unsigned long long *keys;   // [max_batch]
+    unsigned int *arrivals;     // [max_batch]
+    unsigned int *err;          // one word
+    int4 *zero16;               // 16 zero bytes
+    int32_t *store;             // [max_batch * pitch] or null
+    int64_t pitch;              // tokens per store row
+    int32_t *store_len;         // [max_batch] or null
+    const int32_t **store_rows; // [max_batch] device row pointers or null
+};
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+pld_status fail(pld_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+
+pld_status fail(pld_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+pld_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(PLD_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+void release(pld_ctx *c)
+{
+    if (!c)
+        return;
+    if (c->keys) (void)hipFree(c->keys);
+    if (c->arrivals) (void)hipFree(c->arrivals);
+    if (c->err) (void)hipFree(c->err);
+    if (c->zero16) (void)hipFree(c->zero16);
+    if (c->store) (void)hipFree(c->store);
+    if (c->store_len) (void)hipFree(c->store_len);
+    if (c->store_rows) (void)hipFree(c->store_rows);
+    delete c;
+}
+
+bool valid_tile(int32_t t)
+{
+    return t == 256 || t == 1024 || t == 2048 || t == 4096 || t == 8192;
+}
+
+pld_status check_draft_args(pld_ctx *ctx, const int32_t *const *histories,
+                            const int32_t *lengths, int32_t batch, int32_t n_min,
+                            int32_t n_max, int32_t k_max, int32_t *out_draft,
+                            int32_t *out_len, int32_t *out_match)
+{
+    if (!ctx)
+        return fail(PLD_EINVAL, "ctx is null");
+    if (n_min < 1 || n_max < n_min || n_max > PLD_N_MAX_LIMIT)
+        return fail(PLD_EINVAL, "need 1 <= n_min <= n_max <= %d (got n_min=%d n_max=%d)",
+                    PLD_N_MAX_LIMIT, n_min, n_max);
+    if (k_max < 1)
+        return fail(PLD_EINVAL, "k_max must be >= 1 (got %d)", k_max);
+    if (batch < 0 || batch > ctx->max_batch)
+        return fail(PLD_EINVAL, "batch %d outside [0, max_batch=%d]", batch, ctx->max_batch);
+    if (batch > 0 && (!histories || !lengths || !out_draft || !out_len || !out_match))
+        return fail(PLD_EINVAL, "null buffer pointer");
+    if ((int64_t)batch * k_max > INT64_MAX / 4)
+        return fail(PLD_EINVAL, "batch * k_max too large");
+    if (pld::scan_grid(ctx->max_len, batch, ctx->tile_tokens) > 0x7fffffffLL)
+        return fail(PLD_EINVAL, "grid too large: batch %d x tiles for max_len %d", batch,
+                    ctx->max_len);
+    return PLD_OK;
+}
+
+pld_status draft(pld_ctx *ctx, const int32_t *const *histories, const int32_t *lengths,
+                 int32_t batch, int32_t n_min, int32_t n_max, int32_t k_max,
+                 int32_t *out_draft, int32_t *out_len, int32_t *out_match,
+                 int32_t *out_pos, hipStream_t stream)
+{
+    pld_status s = check_draft_args(ctx, histories, lengths, batch, n_min, n_max, k_max,
+                                    out_draft, out_len, out_match);
+    if (s != PLD_OK)
+        return s;
+    if (batch == 0)
+        return PLD_OK;
+    pld::DraftArgs a;
+    a.histories = histories;
+    a.lengths = lengths;
+    a.batch = batch;
+    a.n_min = n_min;
+    a.n_max = n_max;
+    a.k_max = k_max;
+    a.max_len = ctx->max_len;
+    a.fused = ctx->fused;
+    a.out_draft = out_draft;
+    a.out_len = out_len;
+    a.out_match = out_match;
+    a.out_pos = out_pos;
+    a.keys = ctx->keys;
+    a.arrivals = ctx->arrivals;
+    a.err = ctx->err;
+    a.zero16 = ctx->zero16;
+    hipError_t e = pld::launch_draft(a, ctx->tile_tokens, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "draft kernel launch");
+    return PLD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pld_status pld_create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t own_store)
+{
+    if (!out)
+        return fail(PLD_EINVAL, "out is null");
+    if (max_batch < 1)
+        return fail(PLD_EINVAL, "max_batch must be >= 1 (got %d)", max_batch);
+    if (max_len < 1)
+        return fail(PLD_EINVAL, "max_len must be in [1, 2^31-1] (got %d)", max_len);
+    pld_ctx *c = new (std::nothrow) pld_ctx();
+    if (!c)
+        return fail(PLD_ENOMEM, "host allocation failed");
+    memset(c, 0, sizeof(*c));
+    c->max_batch = max_batch;
+    c->max_len = max_len;
+    c->tile_tokens = 4096;
+    c->fused = 1;
+    hipError_t e = hipGetDevice(&c->device);
+    if (e != hipSuccess) {
+        release(c);
+        return hip_fail(e, "hipGetDevice");
+    }
+    const size_t nb = (size_t)max_batch;
+    if (hipMalloc((void **)&c->keys, nb * sizeof(unsigned long long)) != hipSuccess ||
+        hipMalloc((void **)&c->arrivals, nb * sizeof(unsigned int)) != hipSuccess ||
+        hipMalloc((void **)&c->err, sizeof(unsigned int)) != hipSuccess ||
+        hipMalloc((void **)&c->zero16, sizeof(int4)) != hipSuccess) {
+        (void)hipGetLastError();
+        release(c);
+        return fail(PLD_ENOMEM, "device allocation of reduction slots failed");
+    }
+    if (own_store) {
+        c->pitch = ((int64_t)max_len + 63) / 64 * 64;
+        const double bytes = (double)nb * (double)c->pitch * 4.0;
+        if (bytes > 9.0e18 ||
+            hipMalloc((void **)&c->store, nb * (size_t)c->pitch * sizeof(int32_t)) != hipSuccess ||
+            hipMalloc((void **)&c->store_len, nb * sizeof(int32_t)) != hipSuccess ||
+            hipMalloc((void **)&c->store_rows, nb * sizeof(int32_t *)) != hipSuccess) {
+            (void)hipGetLastError();
+            release(c);
+            return fail(PLD_ENOMEM, "device allocation of the %d x %d token store failed",
+                        max_batch, max_len);
+        }
+    }
+    e = hipMemset(c->keys, 0, nb * sizeof(unsigned long long));
+    if (e == hipSuccess) e = hipMemset(c->arrivals, 0, nb * sizeof(unsigned int));
+    if (e == hipSuccess) e = hipMemset(c->err, 0, sizeof(unsigned int));
+    if (e == hipSuccess) e = hipMemset(c->zero16, 0, sizeof(int4));
+    if (e == hipSuccess && own_store) {
+        e = hipMemset(c->store_len, 0, nb * sizeof(int32_t));
+        const int32_t **rows = new (std::nothrow) const int32_t *[nb];
+        if (!rows) {
+            release(c);
+            return fail(PLD_ENOMEM, "host allocation failed");
+        }
+        for (size_t b = 0; b < nb; ++b)
+            rows[b] = c->store + (int64_t)b * c->pitch;
+        if (e == hipSuccess)
+            e = hipMemcpy(c->store_rows, rows, nb * sizeof(int32_t *), hipMemcpyHostToDevice);
+        delete[] rows;
+    }
+    if (e == hipSuccess)
+        e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        release(c);
+        return hip_fail(e, "context initialisation");
+    }
+    *out = c;
+    return PLD_OK;
+}
+
+pld_status pld_destroy(pld_ctx *ctx)
+{
+    if (!ctx)
+        return PLD_OK;
+    hipError_t e = hipDeviceSynchronize();
+    release(ctx);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipDeviceSynchronize before destroy");
+    return PLD_OK;
+}
+
+pld_status pld_configure(pld_ctx *ctx, int32_t tile_tokens, int32_t fused_gather)
+{
+    if (!ctx)
+        return fail(PLD_EINVAL, "ctx is null");
+    if (tile_tokens != 0 && !valid_tile(tile_tokens))
+        return fail(PLD_EINVAL, "tile_tokens %d not one of 256, 1024, 2048, 4096, 8192",
+                    tile_tokens);
+    if (fused_gather < -1 || fused_gather > 1)
+        return fail(PLD_EINVAL, "fused_gather must be -1, 0 or 1 (got %d)", fused_gather);
+    if (tile_tokens != 0)
+        ctx->tile_tokens = tile_tokens;
+    if (fused_gather >= 0)
+        ctx->fused = fused_gather;
+    return PLD_OK;
+}
+
+pld_status pld_append(pld_ctx *ctx, const int32_t *tokens, int64_t tokens_stride,
+                      const int32_t *counts, int32_t batch, hipStream_t stream)
+{
+    if (!ctx)
+        return fail(PLD_EINVAL, "ctx is null");
+    if (!ctx->store)
+        return fail(PLD_EINVAL, "context was created without a store");
+    if (batch < 0 || batch > ctx->max_batch)
+        return fail(PLD_EINVAL, "batch %d outside [0, max_batch=%d]", batch, ctx->max_batch);
+    if (tokens_stride < 0)
+        return fail(PLD_EINVAL, "tokens_stride must be >= 0");
+    if (batch == 0)
+        return PLD_OK;
+    if (!tokens || !counts)
+        return fail(PLD_EINVAL, "null buffer pointer");
+    pld::AppendArgs a;
+    a.tokens = tokens;
+    a.tokens_stride = tokens_stride;
+    a.counts = counts;
+    a.store = ctx->store;
+    a.pitch = ctx->pitch;
+    a.lengths = ctx->store_len;
+    a.max_len = ctx->max_len;
+    a.err = ctx->err;
+    hipError_t e = pld::launch_append(a, batch, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "append kernel launch");
+    return PLD_OK;
+}
+
+pld_status pld_store_views(pld_ctx *ctx, const int32_t *const **histories,
+                           const int32_t **lengths)
+{
+    if (!ctx || !histories || !lengths)
+        return fail(PLD_EINVAL, "null argument");
+    if (!ctx->store)
+        return fail(PLD_EINVAL, "context was created without a store");
+    *histories = ctx->store_rows;
+    *lengths = ctx->store_len;
+    return PLD_OK;
+}
+
+pld_status pld_store_reset(pld_ctx *ctx, hipStream_t stream)
+{
+    if (!ctx)
+        return fail(PLD_EINVAL, "ctx is null");
+    if (!ctx->store)
+        return fail(PLD_EINVAL, "context was created without a store");
+    hipError_t e = pld::launch_fill(ctx->store_len, ctx->max_batch, 0, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "store reset launch");
+    return PLD_OK;
+}
+
+pld_status pld_draft_batch(pld_ctx *ctx, const int32_t *const *histories,
+                           const int32_t *lengths, int32_t batch, int32_t n_min,
+                           int32_t n_max, int32_t k_max, int32_t *out_draft,
+                           int32_t *out_len, int32_t *out_match, hipStream_t stream)
+{
+    return draft(ctx, histories, lengths, batch, n_min, n_max, k_max, out_draft, out_len,
+                 out_match, nullptr, stream);
+}
+
+pld_status pld_draft_batch_pos(pld_ctx *ctx, const int32_t *const *histories,
+                               const int32_t *lengths, int32_t batch, int32_t n_min,
+                               int32_t n_max, int32_t k_max, int32_t *out_draft,
+                               int32_t *out_len, int32_t *out_match, int32_t *out_pos,
+                               hipStream_t stream)
+{
+    if (batch > 0 && !out_pos)
+        return fail(PLD_EINVAL, "out_pos is null");
+    return draft(ctx, histories, lengths, batch, n_min, n_max, k_max, out_draft, out_len,
+                 out_match, out_pos, stream);
+}
+
+pld_status pld_sync(pld_ctx *ctx, hipStream_t stream)
+{
+    if (!ctx)
+        return fail(PLD_EINVAL, "ctx is null");
+    unsigned int bits = 0;
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e == hipSuccess)
+        e = hipMemcpy(&bits, ctx->err, sizeof(bits), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && bits)
+        e = hipMemset(ctx->err, 0, sizeof(unsigned int));
+    if (e == hipSuccess)
+        e = hipDeviceSynchronize();
+    if (e != hipSuccess)
+        return hip_fail(e, "pld_sync");
+    if (bits & (pld::kErrLenCapacity | pld::kErrAppendCapacity))
+        return fail(PLD_ECAPACITY, "device reported: %s%s",
+                    (bits & pld::kErrLenCapacity) ? "a history longer than max_len " : "",
+                    (bits & pld::kErrAppendCapacity) ? "an append past max_len" : "");
+    if (bits)
+        return fail(PLD_EINVAL, "device reported: %s%s%s",
+                    (bits & pld::kErrLenNegative) ? "a negative length " : "",
+                    (bits & pld::kErrBadRow) ? "a null or misaligned row pointer " : "",
+                    (bits & pld::kErrAppendNegative) ? "a negative append count" : "");
+    return PLD_OK;
+}
+
+const char *pld_strerror(pld_status status)
+{
+    switch (status) {
+    case PLD_OK: return "success";
+    case PLD_EINVAL: return "invalid argument";
+    case PLD_ENOMEM: return "out of device memory";
+    case PLD_EHIP: return "HIP runtime error";
+    case PLD_ECAPACITY: return "history capacity exceeded";
+    }
+    return "unknown status";
+}
+
+const char *pld_last_error(void)
+{
+    return g_last_error;
+}
+
+}  // extern "C"

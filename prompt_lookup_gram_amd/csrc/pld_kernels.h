@@ -1,0 +1,61 @@
+// Internal interface between the C-ABI layer (pld_api.cpp) and the HIP
+// kernels (pld_kernels.hip). Not installed; callers use include/pld.h.
+#ifndef PLD_KERNELS_H_
+#define PLD_KERNELS_H_
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+#include <hip/hip_vector_types.h>
+
+#include "pld.h"
+
+namespace pld {
+
+// Sticky device-side error bits (the context's error word).
+enum : uint32_t {
+    kErrLenCapacity = 1u,     // lengths[b] > max_len
+    kErrLenNegative = 2u,     // lengths[b] < 0
+    kErrBadRow = 4u,          // null or misaligned row pointer with L > 0
+    kErrAppendCapacity = 8u,  // append would pass max_len
+    kErrAppendNegative = 16u  // counts[b] < 0
+};
+
+struct DraftArgs {
+    const int32_t *const *histories;
+    const int32_t *lengths;
+    int32_t batch;
+    int32_t n_min, n_max, k_max;
+    int32_t max_len;
+    int32_t fused;
+    int32_t *out_draft;
+    int32_t *out_len;
+    int32_t *out_match;
+    int32_t *out_pos;              // may be null
+    unsigned long long *keys;      // [max_batch], zero between calls
+    unsigned int *arrivals;        // [max_batch], zero between calls
+    unsigned int *err;             // sticky error word
+    const int4 *zero16;            // 16 zero bytes (edge-chunk load target)
+};
+
+struct AppendArgs {
+    const int32_t *tokens;
+    int64_t tokens_stride;
+    const int32_t *counts;
+    int32_t *store;
+    int64_t pitch;
+    int32_t *lengths;
+    int32_t max_len;
+    unsigned int *err;
+};
+
+// Workgroups the scan launches for a batch (tiles per request x batch).
+int64_t scan_grid(int32_t max_len, int32_t batch, int tile_tokens);
+
+hipError_t launch_draft(const DraftArgs &a, int tile_tokens, hipStream_t s);
+hipError_t launch_append(const AppendArgs &a, int32_t batch, hipStream_t s);
+hipError_t launch_fill(int32_t *p, int64_t n, int32_t value, hipStream_t s);
+
+}  // namespace pld
+
+#endif  // PLD_KERNELS_H_

@@ -1,0 +1,81 @@
+"""The C-ABI library builds, loads and exports every symbol include/pld.h
+declares, and rejects bad arguments on the host before touching the GPU
+(these tests make no compute call and need no GPU)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from prompt_lookup_gram_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "pld.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pld_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_symbols() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_library_is_gfx950_hip_code():
+    data = open(B.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+    assert b"pld_scan" in data
+
+
+def test_strerror_strings():
+    assert B.pld_strerror(B.PLD_OK) == "success"
+    assert B.pld_strerror(B.PLD_EINVAL) == "invalid argument"
+    assert B.pld_strerror(B.PLD_ECAPACITY) == "history capacity exceeded"
+    assert B.pld_strerror(99) == "unknown status"
+
+
+def _raw(fn, *args):
+    return getattr(B.load(), fn)(*args)
+
+
+def test_null_context_rejected():
+    assert _raw("pld_draft_batch", None, None, None, 0, 4, 12, 16, None, None,
+                None, None) == B.PLD_EINVAL
+    assert "ctx is null" in B.pld_last_error()
+    assert _raw("pld_append", None, None, 0, None, 0, None) == B.PLD_EINVAL
+    assert _raw("pld_configure", None, 4096, 1) == B.PLD_EINVAL
+    assert _raw("pld_sync", None, None) == B.PLD_EINVAL
+    assert _raw("pld_store_reset", None, None) == B.PLD_EINVAL
+    assert _raw("pld_destroy", None) == B.PLD_OK
+
+
+@pytest.mark.parametrize("max_batch,max_len,msg", [(0, 10, "max_batch"),
+                                                   (-3, 10, "max_batch"),
+                                                   (4, 0, "max_len"),
+                                                   (4, -1, "max_len")])
+def test_create_rejects_bad_sizes_before_any_hip_call(max_batch, max_len, msg):
+    ctx = ctypes.c_void_p()
+    assert _raw("pld_create", ctypes.byref(ctx), max_batch, max_len, 0) == B.PLD_EINVAL
+    assert msg in B.pld_last_error()
+    assert ctx.value is None
+
+
+def test_create_rejects_null_out():
+    assert _raw("pld_create", None, 4, 10, 0) == B.PLD_EINVAL
+
+
+def test_python_wrapper_raises_with_detail():
+    with pytest.raises(B.PldError) as e:
+        B.pld_create(0, 5)
+    assert e.value.status == B.PLD_EINVAL and "max_batch" in str(e.value)
