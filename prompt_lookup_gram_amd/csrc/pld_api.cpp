@@ -20,8 +20,7 @@ struct pld_ctx {
     int32_t max_len;
     int32_t tile_tokens;
     int32_t fused;
-    unsigned long long *keys;   // [max_batch]
-    unsigned int *arrivals;     // [max_batch]
+    pld::ReqSlot *slots;        // [max_batch] reduction state
     unsigned int *err;          // one word
     int4 *zero16;               // 16 zero bytes
     int32_t *store;             // [max_batch * pitch] or null
@@ -54,8 +53,7 @@ void release(pld_ctx *c)
 {
     if (!c)
         return;
-    if (c->keys) (void)hipFree(c->keys);
-    if (c->arrivals) (void)hipFree(c->arrivals);
+    if (c->slots) (void)hipFree(c->slots);
     if (c->err) (void)hipFree(c->err);
     if (c->zero16) (void)hipFree(c->zero16);
     if (c->store) (void)hipFree(c->store);
@@ -117,8 +115,7 @@ pld_status draft(pld_ctx *ctx, const int32_t *const *histories, const int32_t *l
     a.out_len = out_len;
     a.out_match = out_match;
     a.out_pos = out_pos;
-    a.keys = ctx->keys;
-    a.arrivals = ctx->arrivals;
+    a.slots = ctx->slots;
     a.err = ctx->err;
     a.zero16 = ctx->zero16;
     hipError_t e = pld::launch_draft(a, ctx->tile_tokens, stream);
@@ -153,8 +150,7 @@ pld_status pld_create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t
         return hip_fail(e, "hipGetDevice");
     }
     const size_t nb = (size_t)max_batch;
-    if (hipMalloc((void **)&c->keys, nb * sizeof(unsigned long long)) != hipSuccess ||
-        hipMalloc((void **)&c->arrivals, nb * sizeof(unsigned int)) != hipSuccess ||
+    if (hipMalloc((void **)&c->slots, nb * sizeof(pld::ReqSlot)) != hipSuccess ||
         hipMalloc((void **)&c->err, sizeof(unsigned int)) != hipSuccess ||
         hipMalloc((void **)&c->zero16, sizeof(int4)) != hipSuccess) {
         (void)hipGetLastError();
@@ -174,8 +170,7 @@ pld_status pld_create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t
                         max_batch, max_len);
         }
     }
-    e = hipMemset(c->keys, 0, nb * sizeof(unsigned long long));
-    if (e == hipSuccess) e = hipMemset(c->arrivals, 0, nb * sizeof(unsigned int));
+    e = hipMemset(c->slots, 0, nb * sizeof(pld::ReqSlot));
     if (e == hipSuccess) e = hipMemset(c->err, 0, sizeof(unsigned int));
     if (e == hipSuccess) e = hipMemset(c->zero16, 0, sizeof(int4));
     if (e == hipSuccess && own_store) {

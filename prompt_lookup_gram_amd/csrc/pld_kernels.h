@@ -21,6 +21,15 @@ enum : uint32_t {
     kErrAppendNegative = 16u  // counts[b] < 0
 };
 
+// Per-request reduction state: the packed key maximum and the arrival
+// counter of the fused gather. One slot per 256 bytes, so that atomics of
+// different requests fall on different cache lines. Zero between calls.
+struct alignas(256) ReqSlot {
+    unsigned long long key;
+    unsigned int arrivals;
+    unsigned int pad[61];
+};
+
 struct DraftArgs {
     const int32_t *const *histories;
     const int32_t *lengths;
@@ -32,8 +41,7 @@ struct DraftArgs {
     int32_t *out_len;
     int32_t *out_match;
     int32_t *out_pos;              // may be null
-    unsigned long long *keys;      // [max_batch], zero between calls
-    unsigned int *arrivals;        // [max_batch], zero between calls
+    ReqSlot *slots;                // [max_batch], zero between calls
     unsigned int *err;             // sticky error word
     const int4 *zero16;            // 16 zero bytes (edge-chunk load target)
 };

@@ -18,24 +18,33 @@
 // maxima are merged with a 64-bit atomicMax; the result does not depend on
 // the tiling or on the order workgroups run in.
 //
-// pld_scan (one workgroup per tile of TILE candidate end positions):
-//   1. Coalesced 16-byte loads bring the tile, plus HALO tokens to its left,
-//      into registers; rows that are not 16-byte aligned are handled by
-//      addressing aligned 16-byte chunks and shifting by the misalignment.
-//   2. First-token rejection in registers: only positions holding the
-//      history's last token survive (about 2-3% on Zipf text).
-//   3. The registers are staged into LDS; survivors extend backwards from
-//      LDS against the suffix (also in LDS) up to m tokens.
-//   4. Per-thread max -> wavefront max (cross-lane shuffles on 2x32-bit) ->
-//      workgroup max (LDS) -> 64-bit atomicMax into the request's slot when
-//      the request spans more than one tile.
-//   5. Fused gather: the last workgroup of a request to arrive (an agent-scope
-//      acquire-release counter) decodes the key, writes the draft row, and
-//      clears the request's slot and counter for the next call.
+// pld_scan (one workgroup per tile of TILE candidate end positions; each
+// wavefront takes a contiguous share of the tile and works on its own):
+//   1. Coalesced, non-temporal 16-byte loads bring the wavefront's span plus
+//      the 64 tokens to its left into registers; rows that are not 16-byte
+//      aligned are read as aligned chunks shifted by the misalignment.
+//   2. The registers are staged in the wavefront's own LDS region.
+//   3. Rejection in registers: a position survives only if it holds the
+//      history's last token (about 2-4% on Zipf text) and, when n_min >= 3,
+//      its two predecessors hold the two tokens before that (the tokens
+//      before a chunk come from the neighbouring lane by a DPP wavefront
+//      shift); survivors extend backwards from LDS up to m tokens, several
+//      tokens per LDS round trip.
+//   4. Per-thread max -> wavefront max (DPP row shifts and broadcasts on
+//      2x32-bit halves), only in wavefronts that found a match, then either
+//      a 64-bit atomicMax into the request's slot per wavefront (separate
+//      gather kernel), or a workgroup max (LDS atomic) and the fused gather.
+//   5. Fused gather: each workgroup of a multi-tile request merges its max
+//      with a 64-bit atomicMax and counts itself in with an atomic add; the
+//      last one to arrive takes the maximum with an atomic exchange (which
+//      also clears the slot for the next call), writes the draft row and
+//      clears the counter. Single-tile requests emit directly.
 // pld_gather is the same step 5 as its own kernel, for the unfused mode.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "pld_kernels.h"
 
@@ -46,17 +55,38 @@ namespace {
 constexpr int kHalo = 64;                 // >= PLD_N_MAX_LIMIT - 1, multiple of 4
 constexpr int kHaloChunks = kHalo / 4;    // 16-byte chunks of halo
 constexpr int kWave = 64;
+constexpr int kExtBlock = 4;             // tokens compared per LDS round trip when extending
 
 typedef unsigned long long u64;
 
+// One step of a wavefront maximum over 64-bit keys: each lane takes the max
+// of its value and the value DPP control `ctrl` routes to it (the two 32-bit
+// halves move separately). Lanes left out by the row/bank masks, or whose
+// source is outside the wavefront, see 0, which leaves a maximum unchanged.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ u64 dpp_max_step(u64 v)
+{
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, ROW_MASK, BANK_MASK, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, ROW_MASK, BANK_MASK, false);
+    const u64 o = ((u64)hi << 32) | lo;
+    return o > v ? o : v;
+}
+
+// Maximum over the wavefront, delivered in lane 63: shifts by 1, 2 and 3
+// within each row of 16 lanes, then by 4 and 8 in the upper banks, then the
+// row-15 and row-31 broadcasts carry the partial maxima across rows.
 __device__ __forceinline__ u64 wave_max_u64(u64 v)
 {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-        const u64 o = __shfl_xor(v, off, kWave);
-        v = o > v ? o : v;
-    }
-    return v;
+    v = dpp_max_step<0x111, 0xf, 0xf>(v);  // row_shr:1
+    v = dpp_max_step<0x112, 0xf, 0xf>(v);  // row_shr:2
+    v = dpp_max_step<0x113, 0xf, 0xf>(v);  // row_shr:3
+    v = dpp_max_step<0x114, 0xf, 0xe>(v);  // row_shr:4, banks 1-3
+    v = dpp_max_step<0x118, 0xf, 0xc>(v);  // row_shr:8, banks 2-3
+    v = dpp_max_step<0x142, 0xa, 0xf>(v);  // row_bcast:15, rows 1 and 3
+    v = dpp_max_step<0x143, 0xc, 0xf>(v);  // row_bcast:31, rows 2 and 3
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, kWave - 1);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), kWave - 1);
+    return ((u64)hi << 32) | lo;
 }
 
 // Loads through the global address space (global_load_* rather than
@@ -70,10 +100,14 @@ __device__ __forceinline__ T gld(const T *p)
 
 typedef int32_t v4i32 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int4 gld(const int4 *p)
+
+// Streaming load of history data, read once per call: marked non-temporal
+// so it does not push the kernel's own code and the small shared arrays out
+// of the L2.
+__device__ __forceinline__ int4 gld_stream(const int4 *p)
 {
     typedef __attribute__((address_space(1))) const v4i32 gV;
-    const v4i32 x = *(gV *)p;
+    const v4i32 x = __builtin_nontemporal_load((gV *)p);
     return make_int4(x[0], x[1], x[2], x[3]);
 }
 
@@ -154,20 +188,216 @@ __device__ __forceinline__ int4 patch_chunk(int4 v, int64_t p0, const int32_t *h
     return v;
 }
 
+// Wait until every memory operation this wave issued has completed (for an
+// atomic: has been performed), before issuing the next one.
+__device__ __forceinline__ void wait_vm()
+{
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), expcnt/lgkmcnt unconstrained
+}
+
+// Scans this wavefront's share of one tile and returns the lane's best key.
+//
+// A workgroup's tile of TILE candidate end positions [t0, t0 + TILE) is cut
+// into one contiguous span per wavefront (kSpan 16-byte chunks). Each
+// wavefront works alone, with no workgroup barrier: it loads its span plus
+// the kHalo tokens before it (and, for the last wavefront, the chunk after
+// it, which holds the tile's last positions when the row is not 16-byte
+// aligned) and stages them in its own LDS region. Lane l holds chunks
+// l, 64 + l, 128 + l, ... of the span, so each load instruction reads 1 KiB
+// of consecutive bytes.
+//
+// FILTER3 (n_min >= 3): a position survives the register test only if its
+// token and the two before it equal the suffix's last three tokens; the
+// tokens before a chunk come from the lane to the left (DPP wavefront shift)
+// or, for lane 0, from the previous slot's lane 63 or the halo. A rejected
+// position matches fewer than 3 <= n_min tokens, so it can never produce a
+// key. Otherwise only the first token is tested. Survivors extend backwards
+// from LDS up to m tokens.
+// CHECKED (the first and last tile of a request): loads stay inside the row
+// and every position is range-checked; interior tiles skip both.
+template <int TILE, int THREADS, bool CHECKED, bool FILTER3>
+__device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64_t t0,
+                                         int32_t mhat, int4 *lds_win, int32_t *lds_pat)
+{
+    constexpr int kWaves = THREADS / kWave;
+    constexpr int kSpan = TILE / 4 / kWaves;         // chunks per wavefront
+    constexpr int kPer = kSpan / kWave;              // chunks per lane
+    constexpr int kWinW = kHaloChunks + kSpan + 1;   // per-wavefront window
+    static_assert(kSpan % kWave == 0, "whole chunks per lane");
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid & (kWave - 1);
+    const bool last_wave = wave == kWaves - 1;
+    int4 *win = lds_win + wave * kWinW;
+    int32_t *pat = lds_pat + wave * kWave;
+
+    const int32_t nrel = (int32_t)(((int64_t)r.ncand - t0) < TILE ? (r.ncand - t0) : TILE);
+    const int delta = (int)(((uintptr_t)r.h >> 2) & 3u);
+    const int4 *arow = (const int4 *)(r.h - delta);
+    // local chunk q of this wavefront is tile-window chunk wave * kSpan + q;
+    // tile-window chunk 0 starts kHalo + delta tokens before t0.
+    const int64_t gq0 = (t0 - kHalo) / 4 + (int64_t)wave * kSpan;  // exact
+    const int64_t pq0 = t0 - kHalo - delta + 4 * (int64_t)wave * kSpan;  // position of local token 0
+    const int32_t rq0 = (int32_t)(pq0 - t0);  // rel (position - t0) of local token 0
+    // the extra chunk: halo (lanes 0..15), the chunk after the span (lane 16)
+    const int qx = lane < kHaloChunks ? lane : (lane == kHaloChunks ? kHaloChunks + kSpan : -1);
+
+    // 1. loads, all issued back to back with no branch in between (a load
+    // inside a branch makes the compiler wait for it at the join). Lanes
+    // without an extra chunk re-read their first chunk; lanes past the
+    // suffix length re-read its first token.
+    const int32_t p1 = gld(r.h + r.L - 1);
+    const int32_t p2 = gld(r.h + r.L - 2);  // L >= 2 whenever a tile is scanned
+    const int32_t p3 = gld(r.h + r.L - (mhat >= 3 ? 3 : 1));
+    const int32_t pv = gld(r.h + r.L - mhat + (lane < mhat ? lane : 0));
+    int4 v[kPer + 1];
+    if constexpr (!CHECKED) {
+        // the extra chunk first: slot 0's tests need the halo
+        v[kPer] = gld_stream(arow + (gq0 + (qx >= 0 ? qx : kHaloChunks + lane)));
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+            v[k] = gld_stream(arow + (gq0 + kHaloChunks + k * kWave + lane));
+    } else {
+        bool inside[kPer + 1];
+#pragma unroll
+        for (int k = 0; k <= kPer; ++k) {
+            const int q = k < kPer ? kHaloChunks + k * kWave + lane : qx;
+            inside[k] = q >= 0 && chunk_inside(pq0 + 4 * q, r.L);
+            v[k] = gld_stream(inside[k] ? arow + (gq0 + q) : a.zero16);
+        }
+#pragma unroll
+        for (int k = 0; k <= kPer; ++k) {
+            const int q = k < kPer ? kHaloChunks + k * kWave + lane : qx;
+            if (q >= 0 && !inside[k])
+                v[k] = patch_chunk(v[k], pq0 + 4 * q, r.h, r.L);
+        }
+    }
+
+    // 2. stage the window and the suffix in this wavefront's LDS region
+    // (DS operations of one wavefront complete in order, so no barrier).
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        win[kHaloChunks + k * kWave + lane] = v[k];
+    if (qx >= 0)
+        win[qx] = v[kPer];
+    pat[lane] = pv;  // slots >= mhat are unused
+    __builtin_amdgcn_wave_barrier();
+
+    // 3. rejection tests. Bit 4k + i of `bits` says token i of slot k (slot
+    // kPer: the extra chunk) goes on to extend.
+    static_assert(4 * (kPer + 1) <= 64, "survivor bitmask is 64 bits");
+    typedef typename std::conditional<4 * (kPer + 1) <= 32, uint32_t, u64>::type mask_t;
+    mask_t bits = 0;
+    // Positions owned by this wavefront: rel in [lo, hi). The span's
+    // positions belong to it, the chunk after the span only to the last
+    // wavefront; with the 3-token filter positions 0 and 1 are left out (a
+    // match ending there has fewer than 3 tokens, below n_min).
+    const int32_t lo = FILTER3 ? (t0 < 2 ? 2 - (int32_t)t0 : 0) : 0;
+    const int32_t span_end = rq0 + 4 * (kHaloChunks + kSpan);
+    const int32_t hi = last_wave ? nrel : (span_end < nrel ? span_end : nrel);
+    const int32_t ell0 = FILTER3 ? 3 : 1;  // tokens known to match for a survivor
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int32_t r0 = rq0 + 4 * (kHaloChunks + k * kWave + lane);  // rel of token 0
+        bool c[4];
+        if constexpr (FILTER3) {
+            // the two tokens before this chunk
+            int32_t pz = __builtin_amdgcn_mov_dpp(v[k].z, 0x138 /* wave_shr:1 */, 0xf, 0xf, true);
+            int32_t pw = __builtin_amdgcn_mov_dpp(v[k].w, 0x138 /* wave_shr:1 */, 0xf, 0xf, true);
+            const int32_t lz = k > 0 ? __builtin_amdgcn_readlane(v[k - 1].z, kWave - 1)
+                                     : __builtin_amdgcn_readlane(v[kPer].z, kHaloChunks - 1);
+            const int32_t lw = k > 0 ? __builtin_amdgcn_readlane(v[k - 1].w, kWave - 1)
+                                     : __builtin_amdgcn_readlane(v[kPer].w, kHaloChunks - 1);
+            pz = lane == 0 ? lz : pz;
+            pw = lane == 0 ? lw : pw;
+            c[0] = v[k].x == p1 && pw == p2 && pz == p3;
+            c[1] = v[k].y == p1 && v[k].x == p2 && pw == p3;
+            c[2] = v[k].z == p1 && v[k].y == p2 && v[k].x == p3;
+            c[3] = v[k].w == p1 && v[k].z == p2 && v[k].y == p3;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                c[i] = comp(v[k], i) == p1;
+        }
+        // inside an interior tile only wavefront 0's first chunk can hold
+        // positions outside [lo, hi) (the delta tokens before t0)
+        if (CHECKED || k == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                c[i] = c[i] && r0 + i >= lo && (!CHECKED || r0 + i < hi);
+        }
+        bits |= ((mask_t)c[0] | (mask_t)c[1] << 1 | (mask_t)c[2] << 2 | (mask_t)c[3] << 3) << (4 * k);
+    }
+    // the chunk after the span holds the tile's last positions (those of
+    // them the last wavefront owns): tested on the first token only
+    if (last_wave && lane == kHaloChunks) {
+        const int32_t r0 = rq0 + 4 * qx;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            bits |= (mask_t)(r0 + i >= lo && r0 + i < hi && comp(v[kPer], i) == p1) << (4 * kPer + i);
+    }
+
+    // 4. survivors extend backwards from LDS. Most wavefronts have none and
+    // skip this with one branch; otherwise each lane walks its bitmask.
+    u64 best = 0;
+    if (__any(bits != 0)) {
+        const int32_t *wt = (const int32_t *)win;
+        // lowest rel an extension may reach: position 0 (first tile) or the halo
+        const int32_t floor_rel = t0 < kHalo ? -(int32_t)t0 : -kHalo;
+        while (bits) {
+            const int bit = sizeof(mask_t) == 4 ? __builtin_ctz((uint32_t)bits) : __builtin_ctzll((u64)bits);
+            bits &= bits - 1;
+            const int k = bit >> 2, i = bit & 3;
+            const int q = k < kPer ? kHaloChunks + k * kWave + lane : qx;
+            const int32_t slot = 4 * q + i;
+            const int32_t rel = rq0 + slot;
+            int32_t ell = k < kPer ? ell0 : 1;
+            ell = ell < mhat ? ell : mhat;
+            // compare up to kExtBlock further tokens per LDS round trip: the
+            // reads are independent, a mismatch mask marks the first token
+            // that differs (or lies past m or before position 0)
+            const int32_t lim = (!CHECKED || rel - mhat + 1 >= floor_rel) ? mhat : rel - floor_rel + 1;
+            while (ell < lim) {
+                // all reads first (indices clamped into range, no branches),
+                // then the comparisons
+                int32_t tk[kExtBlock], pt[kExtBlock];
+#pragma unroll
+                for (int u = 0; u < kExtBlock; ++u) {
+                    const int32_t j = ell + u < lim ? ell + u : ell;
+                    tk[u] = wt[slot - j];
+                    pt[u] = pat[mhat - 1 - j];
+                }
+                uint32_t miss = 1u << kExtBlock;
+#pragma unroll
+                for (int u = 0; u < kExtBlock; ++u)
+                    miss |= (uint32_t)((tk[u] != pt[u]) | (ell + u >= lim)) << u;
+                const int run = __builtin_ctz(miss);
+                ell += run;
+                if (run < kExtBlock)
+                    break;
+            }
+            if (ell >= a.n_min) {
+                const u64 key = ((u64)(uint32_t)ell << 32) | (uint32_t)(t0 + rel);
+                best = key > best ? key : best;
+            }
+        }
+    }
+    return best;
+}
+
 template <int TILE, int THREADS>
 __global__ __launch_bounds__(THREADS) void pld_scan(DraftArgs a)
 {
-    static_assert(TILE % (4 * THREADS) == 0, "tile must be whole chunks per thread");
-    static_assert(THREADS >= kHaloChunks + 1, "halo needs 17 loader threads");
-    constexpr int kBody = TILE / 4;            // chunks in the tile body
-    constexpr int kPer = kBody / THREADS;      // body chunks per thread
-    constexpr int kWin = kHaloChunks + kBody + 1;
+    static_assert(THREADS % kWave == 0, "whole wavefronts");
+    static_assert(TILE % (4 * THREADS) == 0, "whole chunks per lane");
     constexpr int kWaves = THREADS / kWave;
-    static_assert(4 * (kPer + 1) <= 64, "candidate mask is 64 bits");
+    constexpr int kWinW = kHaloChunks + TILE / 4 / kWaves + 1;
+    static_assert(kWave >= PLD_N_MAX_LIMIT, "one suffix token per lane");
 
-    __shared__ int4 win[kWin];
-    __shared__ int32_t pat[PLD_N_MAX_LIMIT];
-    __shared__ u64 wave_best[kWaves];
+    __shared__ int4 win[kWaves * kWinW];
+    __shared__ int32_t pat[kWaves * kWave];
+    __shared__ u64 wg_best;
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
@@ -182,129 +412,79 @@ __global__ __launch_bounds__(THREADS) void pld_scan(DraftArgs a)
 
     const int32_t mhat = r.L - 1 < a.n_max ? r.L - 1 : a.n_max;
     u64 best = 0;
-
     if (mhat >= a.n_min) {
         const int64_t t0 = (int64_t)tile * TILE;
-        const int32_t nrel = (int32_t)(((int64_t)r.ncand - t0) < TILE ? (r.ncand - t0) : TILE);
-        const int32_t last = gld(r.h + r.L - 1);
-        const int delta = (int)(((uintptr_t)r.h >> 2) & 3u);
-        const int4 *arow = (const int4 *)(r.h - delta);
-        const int64_t gc0 = (t0 - kHalo) / 4;  // exact: t0 and kHalo are multiples of 4
-        const int64_t p_base = t0 - kHalo - delta;  // position of window token 0
-
-        // 1. loads: kPer body chunks, plus one halo/spill chunk for 17 threads
-        // window chunk of body slot k is kHaloChunks + k * THREADS + tid; the
-        // extra slot kPer is a halo chunk (tid < 16), the spill chunk past
-        // the body (tid == 16, used when the row is not 16-byte aligned) or
-        // nothing (wx < 0).
-        const int wx = tid < kHaloChunks ? tid : (tid == kHaloChunks ? kHaloChunks + kBody : -1);
-        int4 v[kPer + 1];
-        bool inside[kPer + 1];
-#pragma unroll
-        for (int k = 0; k <= kPer; ++k) {
-            const int wk = k < kPer ? kHaloChunks + k * THREADS + tid : wx;
-            inside[k] = wk >= 0 && chunk_inside(p_base + 4 * wk, r.L);
-            const int4 *src = inside[k] ? arow + (gc0 + wk) : a.zero16;
-            v[k] = gld(src);
-        }
-        if (tid < mhat)
-            pat[tid] = gld(r.h + r.L - mhat + tid);
-#pragma unroll
-        for (int k = 0; k <= kPer; ++k) {
-            const int wk = k < kPer ? kHaloChunks + k * THREADS + tid : wx;
-            if (wk >= 0 && !inside[k])
-                v[k] = patch_chunk(v[k], p_base + 4 * wk, r.h, r.L);
-        }
-
-        // 2. first-token rejection on registers. rel = position - t0.
-        u64 cand = 0;
-#pragma unroll
-        for (int k = 0; k <= kPer; ++k) {
-            const int wk = k < kPer ? kHaloChunks + k * THREADS + tid : wx;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int32_t rel = 4 * wk + i - kHalo - delta;
-                const bool hit = wk >= 0 && rel >= 0 && rel < nrel && comp(v[k], i) == last;
-                cand |= (u64)hit << (4 * k + i);
-            }
-        }
-
-        // 3. stage in LDS, then extend the survivors backwards.
-#pragma unroll
-        for (int k = 0; k < kPer; ++k)
-            win[kHaloChunks + k * THREADS + tid] = v[k];
-        if (wx >= 0)
-            win[wx] = v[kPer];
-        __syncthreads();
-
-        const int32_t *wt = (const int32_t *)win;
-        const int32_t floor_rel = t0 < kHalo ? -(int32_t)t0 : -kHalo;  // rel of position 0 (or the halo start)
-        while (cand) {
-            const int bit = __builtin_ctzll(cand);
-            cand &= cand - 1;
-            const int k = bit >> 2, i = bit & 3;
-            const int wk = k < kPer ? kHaloChunks + k * THREADS + tid : wx;
-            const int32_t slot = 4 * wk + i;
-            const int32_t rel = slot - kHalo - delta;
-            int32_t ell = 1;
-            while (ell < mhat && rel - ell >= floor_rel && wt[slot - ell] == pat[mhat - 1 - ell])
-                ++ell;
-            if (ell >= a.n_min) {
-                const u64 key = ((u64)(uint32_t)ell << 32) | (uint32_t)(t0 + rel);
-                best = key > best ? key : best;
-            }
-        }
+        // interior: halo and the chunk after the tile lie inside the row and
+        // every position of the tile is a candidate
+        const bool interior = t0 >= kHalo + 4 && t0 + TILE + 4 <= (int64_t)r.L - 1;
+        const bool f3 = a.n_min >= 3;
+        if (interior)
+            best = f3 ? scan_wave<TILE, THREADS, false, true>(a, r, t0, mhat, win, pat)
+                      : scan_wave<TILE, THREADS, false, false>(a, r, t0, mhat, win, pat);
+        else
+            best = f3 ? scan_wave<TILE, THREADS, true, true>(a, r, t0, mhat, win, pat)
+                      : scan_wave<TILE, THREADS, true, false>(a, r, t0, mhat, win, pat);
     }
 
-    // 4. thread -> wavefront -> workgroup maximum.
-    if (__any(best != 0))
+    // 5. wavefront maximum by DPP (only in wavefronts that found a match),
+    // then lane 0 merges it: into the request's slot (separate gather
+    // kernel) or into the workgroup's LDS slot (fused gather).
+    const bool found = __any(best != 0);
+    if (found)
         best = wave_max_u64(best);
-    if ((tid & (kWave - 1)) == 0)
-        wave_best[tid / kWave] = best;
+    const bool leader = (tid & (kWave - 1)) == 0;
+    if (!a.fused) {
+        // the gather kernel reads the request's slot after this kernel ends
+        if (found && leader)
+            __hip_atomic_fetch_max(&a.slots[b].key, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    if (tid == 0)
+        wg_best = 0;
     __syncthreads();
+    if (found && leader)
+        __hip_atomic_fetch_max(&wg_best, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 
+    // 6. fused gather: the last workgroup of the request to arrive emits the
+    // draft. Only atomic read-modify-writes at agent scope cross
+    // workgroups: each is performed at the location's single point of
+    // coherence, and each workgroup waits for its max to be performed before
+    // it counts itself in, so the workgroup that counts last reads (and
+    // clears) the final maximum with an atomic exchange.
+    __syncthreads();
     if (tid == 0) {
-        u64 m = 0;
-#pragma unroll
-        for (int i = 0; i < kWaves; ++i)
-            m = wave_best[i] > m ? wave_best[i] : m;
-        int last_one = 1;
+        u64 m = wg_best;
+        int last = 1;
         if (r.ntiles > 1) {
-            if (m)
-                __hip_atomic_fetch_max(&a.keys[b], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (a.fused) {
-                const unsigned prev = __hip_atomic_fetch_add(&a.arrivals[b], 1u, __ATOMIC_ACQ_REL,
-                                                             __HIP_MEMORY_SCOPE_AGENT);
-                last_one = prev == (unsigned)(r.ntiles - 1);
-                if (last_one) {
-                    m = __hip_atomic_load(&a.keys[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&a.keys[b], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&a.arrivals[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
+            if (m) {
+                __hip_atomic_fetch_max(&a.slots[b].key, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                wait_vm();
             }
-        } else if (!a.fused && m) {
-            // single-tile request in unfused mode: hand the key to pld_gather
-            __hip_atomic_store(&a.keys[b], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const unsigned prev = __hip_atomic_fetch_add(&a.slots[b].arrivals, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            last = prev == (unsigned)(r.ntiles - 1);
+            if (last) {
+                m = __hip_atomic_exchange(&a.slots[b].key, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_exchange(&a.slots[b].arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
-        wave_best[0] = m;
-        s_last = a.fused && last_one;
+        wg_best = m;
+        s_last = last;
     }
     __syncthreads();
-
-    // 5. fused gather by the last workgroup of the request.
     if (s_last)
-        emit(a, b, r, wave_best[0], tid, THREADS);
+        emit(a, b, r, wg_best, tid, THREADS);
 }
 
 __global__ __launch_bounds__(kWave) void pld_gather(DraftArgs a)
 {
     const int b = blockIdx.x;
     const Req r = load_req(a, b, 1);
-    const u64 key = a.keys[b];
+    const u64 key = a.slots[b].key;
     emit(a, b, r, r.err ? 0ull : key, threadIdx.x, kWave);
     __syncthreads();
     if (threadIdx.x == 0 && key != 0)
-        a.keys[b] = 0;
+        a.slots[b].key = 0;
 }
 
 // One workgroup per request: append counts[b] tokens to store row b.

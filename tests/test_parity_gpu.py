@@ -185,6 +185,30 @@ def test_degenerate_requests():
         assert_parity(w, got, f"n={n_min}..{n_max} k={k_max}")
 
 
+@pytest.mark.parametrize("short", [1, 2, 3])
+@pytest.mark.parametrize("n_min", [1, 2, 3])
+def test_short_best_match_inside_interior_tiles(short, n_min):
+    """The best match is only 1, 2 or 3 tokens long and sits deep inside a
+    long history (an interior tile for every tile size): distinct tokens,
+    with the last `short` tokens planted once more at a middle position
+    behind a different token. Rejection filters must never drop a position
+    whose exact match length can still reach n_min."""
+    rng = np.random.default_rng([31, short, n_min])
+    hs = []
+    for L in (20_000, 50_001, 70_003):
+        h = rng.permutation(10 * L)[:L].astype(np.int32)
+        at = int(rng.integers(L // 3, 2 * L // 3))
+        h[at:at + short] = h[L - short:]
+        hs.append(h)
+    w = wl.Workload("short", hs, n_min, 12, 8)
+    od, ol, om, oj = oracle.draft(hs, n_min, 12, 8)
+    assert om.tolist() == ([short] * 3 if short >= n_min else [0] * 3)
+    for tile in TILES:
+        st, got = run_gpu(w, tile=tile, offsets=rng.integers(0, 4, len(hs)))
+        assert st == B.PLD_OK
+        assert_parity(w, got, f"tile={tile}")
+
+
 def test_periodic_tails_all_periods():
     hs = []
     rng = np.random.default_rng(17)
