@@ -1,19 +1,24 @@
 """Bench: batched prompt-lookup drafting on one MI355X.
 
-A step is one pld_draft_batch call over the whole batch (scan + gather) on the
-16 x 262,144-token workload (Zipf(1.1) documents with a 4,096-token copied
-tail, 0.5% substitutions; n 4..12, k_max 16). Inputs are resident in HBM when
-timing starts.
+A step is one pld_draft_batch call over the whole batch (scan + gather, one
+kernel) on the 16 x 262,144-token workload (Zipf(1.1) documents with a
+4,096-token copied tail, 0.5% substitutions; n 4..12, k_max 16). Inputs are
+resident in HBM when timing starts.
 
 Reported (one JSON line on stdout):
-  value        draft steps/s over the timed region (wall clock around K steps,
-               replayed from HIP graphs of captured calls; each step reads a
-               different one of R copies of the batch, R * 16.8 MB >= 512 MB,
-               so the 256 MB Infinity Cache cannot serve repeats);
-  scan_GBps    4 * sum(L) bytes / mean kernel time (per-launch HIP events);
-  p50_us/p90_us  per-call latency, HIP event pairs around single eager calls;
-  roofline     algorithmic HBM bytes per launch / mean launch time vs 8 TB/s;
-  cpu_baseline the CPU oracle on the same batch (single thread).
+  value         draft steps/s: wall clock around K steps replayed from HIP
+                graphs of captured calls. Each step reads a different one of
+                R copies of the batch (R * 16.8 MB >= 512 MB), so the 256 MB
+                Infinity Cache cannot serve repeats.
+  scan_GBps     4 * sum(L) bytes / the kernel's mean launch time, taken with
+                HIP events around the timed graph replays on the launch
+                stream (one kernel per step).
+  roofline      the same against MI355X's 8 TB/s HBM peak; `traffic` is the
+                HBM bytes per launch from the committed rocprofv3 counter
+                summary, used only while the kernel source still matches it.
+  p50_us/p90_us latency of one call: HIP event pair around a single eager
+                call (this includes the event-pair overhead of the runtime).
+  cpu_baseline  the CPU oracle on the same batch, one thread.
 """
 
 from __future__ import annotations
@@ -33,6 +38,26 @@ if ROOT not in sys.path:
 
 METRIC = ("batched draft steps/s + scanned history GB/s (% HBM peak); "
           "p50 µs per draft step")
+PROFILE = os.path.join(ROOT, "profiles", "pld_scan_c4_b16x262144.md")
+KERNEL_SRC = os.path.join(ROOT, "prompt_lookup_gram_amd", "csrc", "pld_kernels.hip")
+
+
+def profiled_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the kernel source as it is now (else None)."""
+    import hashlib
+    try:
+        text = open(PROFILE).read()
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    sha = traffic = None
+    for line in text.splitlines():
+        if line.startswith("kernel-source-sha256-16:"):
+            sha = line.split(":", 1)[1].strip()
+        if line.startswith("traffic-bytes-per-launch:"):
+            traffic = int(line.split(":", 1)[1].strip())
+    return traffic if sha == src else None
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
 
@@ -42,7 +67,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=4096)
     ap.add_argument("--warmup", type=int, default=256)
-    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4])
+    ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5],
+                    help="workload: 4 (default) is the 16 x 262,144 batch; 1-3 "
+                         "the smaller batches; 5 the 1,024-step streaming decode")
     ap.add_argument("--graph-steps", type=int, default=128,
                     help="draft calls captured per HIP graph")
     ap.add_argument("--latency-calls", type=int, default=2000)
@@ -52,6 +79,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true",
                     help="also time without buffer rotation (cache-resident)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="finish with 8 plain 64 MiB device copies (a counter "
+                         "reference of known size for rocprofv3 --pmc)")
     return ap.parse_args()
 
 
@@ -85,19 +115,27 @@ def main():
     dev = torch.device("cuda:0")
     B.load()
 
+    if args.config == 5:
+        return bench_stream(args, torch, B, wl, dev)
+
     w = wl.ALL_CONFIGS[args.config]()
     bytes_step = 4 * w.total_tokens
     base = B.DeviceBatch(w.histories, device=dev)
-    rot = max(1, -(-2 * MALL_BYTES // bytes_step))
+    # enough copies to defeat the Infinity Cache, capped for the tiny batches
+    # (which are launch-latency bound either way)
+    rot = min(64, max(1, -(-2 * MALL_BYTES // bytes_step)))
     copies = [base] + [base.replicate() for _ in range(rot - 1)]
+    # the row-pointer tables of all copies share one small allocation, as a
+    # serving loop's per-request metadata would; only the histories rotate
+    rows_all = torch.stack([c.rows for c in copies]).contiguous()
     ctx = B.pld_create(w.batch, base.max_len)
     B.pld_configure(ctx, args.tile, args.fused)
     out = B.alloc_outputs(w.batch, w.k_max, device=dev)
 
     def call(i, stream=None):
-        c = copies[i % rot]
-        B.pld_draft_batch(ctx, c.rows, c.lengths, w.batch, w.n_min, w.n_max, w.k_max,
-                          out[0], out[1], out[2], stream=stream)
+        r = i % rot
+        B.pld_draft_batch(ctx, rows_all[r], copies[r].lengths, w.batch, w.n_min,
+                          w.n_max, w.k_max, out[0], out[1], out[2], stream=stream)
 
     # reference output (eager) for the graph check and the parity check
     call(0)
@@ -179,8 +217,17 @@ def main():
     got = [t.cpu().numpy() for t in out[:3]]
     B.pld_destroy(ctx)
 
-    scan_gbps = bytes_step / (mean_us * 1e-6) / 1e9
-    graph_us = gpu_ms * 1e3 / steps
+    if args.calibrate_copy:
+        src = torch.randint(0, 1 << 30, (16 << 20,), dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    graph_us = gpu_ms * 1e3 / steps           # mean launch time (one kernel per step)
+    scan_gbps = bytes_step / (graph_us * 1e-6) / 1e9
+    default_launch = args.tile in (0, 4096) and args.fused in (-1, 1) and args.config == 4
+    traffic = profiled_traffic() if default_launch else None
     rec = {
         "metric": METRIC,
         "value": round(steps_per_s, 1),
@@ -200,18 +247,18 @@ def main():
                    "bytes_per_step": bytes_step, "rotated_copies": rot,
                    "graph_steps": G},
         "request_drafts_per_s": round(steps_per_s * w.batch, 1),
-        "scanned_GBps_step": round(bytes_step / (graph_us * 1e-6) / 1e9, 1),
         "scan_GBps": round(scan_gbps, 1),
         "hbm_frac": round(scan_gbps / HBM_PEAK_GBPS, 4),
         "p50_us": round(p50, 3),
         "p90_us": round(p90, 3),
         "graph_us_per_step": round(graph_us, 3),
+        "eager_call_mean_us": round(mean_us, 3),
         "roofline": {"bound": "hbm", "achieved": round(scan_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(scan_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(scan_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "pld_scan",
-                     "time_source": "mean of per-launch HIP event pairs, "
-                                    f"{n_lat} eager launches, rotated copies"},
+                     "time_source": "HIP events around the timed graph replays "
+                                    f"({steps} launches, rotated copies)"},
     }
     if warm:
         rec["warm"] = warm
@@ -236,6 +283,126 @@ def main():
                       f"{len(os.sched_getaffinity(0))} host cores visible)",
             "effective_GBps": round(bytes_step * n / el / 1e9, 3),
         }
+        rec["parity"] = "bit-exact" if parity else "MISMATCH"
+        if not parity:
+            print(json.dumps(rec))
+            sys.exit(1)
+    print(json.dumps(rec), flush=True)
+
+
+def bench_stream(args, torch, B, wl, dev):
+    """The streaming decode: 64 requests from 32,768 tokens, 1,024 steps of
+    pld_draft_batch on the context's own store, then pld_append of the 1..16
+    tokens each request accepted. The appended tokens follow each request's
+    previous draft while it lasts, then fresh Zipf tokens; they are fixed
+    by one untimed closed-loop pass, then all 1,024 steps are captured in a
+    HIP graph and replayed from the same start state."""
+    start = wl.config5_start()
+    nb, steps_n, width = start.batch, wl.STREAM_STEPS, wl.STREAM_MAX_APPEND
+    ctx = B.pld_create(nb, wl.STREAM_MAX_LEN, own_store=True)
+    rows, lens = B.pld_store_views(ctx)
+    init = torch.from_numpy(np.stack(start.histories)).to(dev)
+    init_counts = torch.full((nb,), wl.STREAM_START_LEN, dtype=torch.int32, device=dev)
+    out = B.alloc_outputs(nb, start.k_max, device=dev)
+
+    def restart():
+        B.pld_store_reset(ctx)
+        B.pld_append(ctx, init, wl.STREAM_START_LEN, init_counts, nb)
+
+    # untimed closed loop: fixes the append stream from the GPU's drafts
+    restart()
+    toks = np.zeros((steps_n, nb, width), np.int32)
+    cnts = np.zeros((steps_n, nb), np.int32)
+    first_drafts = []  # every step's drafts, for the oracle comparison
+    lengths = np.full(nb, wl.STREAM_START_LEN, np.int64)
+    total_tokens = 0
+    for step in range(steps_n):
+        B.pld_draft_batch(ctx, rows, lens, nb, start.n_min, start.n_max, start.k_max,
+                          out[0], out[1], out[2])
+        d, l = out[0].cpu().numpy(), out[1].cpu().numpy()
+        first_drafts.append((d.copy(), l.copy(), out[2].cpu().numpy()))
+        total_tokens += int(lengths.sum())
+        counts, fresh = wl.stream_step_draws(step)
+        toks[step] = wl.compose_append(d, l, counts, fresh)
+        cnts[step] = counts
+        lengths += counts
+        B.pld_append(ctx, torch.from_numpy(toks[step]).to(dev), width,
+                     torch.from_numpy(cnts[step]).to(dev), nb)
+    assert B.pld_sync(ctx) == B.PLD_OK
+    final_ref = [t.clone() for t in out[:3]]
+    toks_d = torch.from_numpy(toks).to(dev)
+    cnts_d = torch.from_numpy(cnts).to(dev)
+
+    # one graph holds all 1,024 steps, in the closed loop's order: draft,
+    # then append the tokens that step accepted
+    cap = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    restart()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=cap):
+        for step in range(steps_n):
+            B.pld_draft_batch(ctx, rows, lens, nb, start.n_min, start.n_max,
+                              start.k_max, out[0], out[1], out[2])
+            B.pld_append(ctx, toks_d[step], width, cnts_d[step], nb)
+    times = []
+    reps = max(1, args.steps // steps_n) if args.steps >= steps_n else 1
+    for rep in range(reps + 1):  # the first replay is warm-up
+        restart()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        for a_, b_ in zip(final_ref, out[:3]):
+            assert torch.equal(a_, b_), "graph replay differs from the closed-loop pass"
+        if rep:
+            times.append((wall, e0.elapsed_time(e1) * 1e-3))
+    assert B.pld_sync(ctx) == B.PLD_OK
+    B.pld_destroy(ctx)
+    wall = float(np.median([t[0] for t in times]))
+    gpu_s = float(np.median([t[1] for t in times]))
+    bytes_mean = 4.0 * total_tokens / steps_n
+    rec = {
+        "metric": METRIC,
+        "value": round(steps_n / wall, 1),
+        "unit": "draft steps/s",
+        "n_gpus": 1,
+        "steps": steps_n * len(times),
+        "warmup": steps_n,
+        "ms_per_step": round(wall * 1e3 / steps_n, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": start.name, "batch": nb, "start_tokens": wl.STREAM_START_LEN,
+                   "steps": steps_n, "n_min": start.n_min, "n_max": start.n_max,
+                   "k_max": start.k_max, "mean_bytes_per_step": round(bytes_mean)},
+        "us_per_step_append_plus_draft": round(gpu_s * 1e6 / steps_n, 3),
+        "scan_GBps": round(bytes_mean * steps_n / gpu_s / 1e9, 1),
+        "hbm_frac": round(bytes_mean * steps_n / gpu_s / 1e9 / HBM_PEAK_GBPS, 4),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        hs = [h.copy() for h in start.histories]
+        n, parity, t_start = 0, True, time.perf_counter()
+        while n < steps_n and time.perf_counter() - t_start < args.cpu_seconds:
+            od, ol, om, _ = oracle.draft(hs, start.n_min, start.n_max, start.k_max)
+            gd, gl, gm = first_drafts[n]
+            parity &= (np.array_equal(od, gd) and np.array_equal(ol, gl)
+                       and np.array_equal(om, gm))
+            hs = oracle.append(hs, toks[n], cnts[n])
+            n += 1
+        el = time.perf_counter() - t_start
+        rec["cpu_baseline"] = {
+            "value": round(n / el, 3), "unit": "draft steps/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the first {n} streaming steps (append + draft, {el:.1f} s, "
+                      f"one thread, {cpu_model()})"}
         rec["parity"] = "bit-exact" if parity else "MISMATCH"
         if not parity:
             print(json.dumps(rec))

@@ -70,7 +70,7 @@ typedef enum pld_status {
  * Create a context for batches of up to max_batch requests whose histories
  * are at most max_len tokens (1 <= max_len <= 2^31 - 1).
  *
- * The context holds 16 bytes of reduction state per request, a sticky error
+ * The context holds 256 bytes of reduction state per request, a sticky error
  * word and, when own_store != 0, a history store of max_batch rows of
  * max_len tokens (row pitch rounded up to 64 tokens) with a length per row,
  * all lengths starting at 0 (fed by pld_append; the Strata prompt-lookup page,
@@ -90,7 +90,7 @@ pld_status pld_destroy(pld_ctx *ctx);
 /*
  * Tuning controls. They never change results, only how the scan is split:
  *  tile_tokens: candidate positions per workgroup, one of 256, 1024, 2048,
- *               4096 (default), 8192; 0 keeps the current value.
+ *               4096 (default), 8192, 16384; 0 keeps the current value.
  *  fused_gather: 1 (default) lets the last workgroup of each request emit
  *               its draft inside the scan kernel; 0 emits drafts with a
  *               second kernel; -1 keeps the current value.

@@ -64,7 +64,7 @@ void release(pld_ctx *c)
 
 bool valid_tile(int32_t t)
 {
-    return t == 256 || t == 1024 || t == 2048 || t == 4096 || t == 8192;
+    return t == 256 || t == 1024 || t == 2048 || t == 4096 || t == 8192 || t == 16384;
 }
 
 pld_status check_draft_args(pld_ctx *ctx, const int32_t *const *histories,
@@ -212,7 +212,7 @@ pld_status pld_configure(pld_ctx *ctx, int32_t tile_tokens, int32_t fused_gather
     if (!ctx)
         return fail(PLD_EINVAL, "ctx is null");
     if (tile_tokens != 0 && !valid_tile(tile_tokens))
-        return fail(PLD_EINVAL, "tile_tokens %d not one of 256, 1024, 2048, 4096, 8192",
+        return fail(PLD_EINVAL, "tile_tokens %d not one of 256, 1024, 2048, 4096, 8192, 16384",
                     tile_tokens);
     if (fused_gather < -1 || fused_gather > 1)
         return fail(PLD_EINVAL, "fused_gather must be -1, 0 or 1 (got %d)", fused_gather);

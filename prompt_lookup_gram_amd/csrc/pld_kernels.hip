@@ -386,9 +386,22 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
     return best;
 }
 
+// The fields needed first are separate leading arguments so that they can be
+// preloaded into SGPRs at wave launch (no scalar load of the kernel
+// arguments before the row table can be read); the rest come in `args`.
 template <int TILE, int THREADS>
-__global__ __launch_bounds__(THREADS) void pld_scan(DraftArgs a)
+__global__ __launch_bounds__(THREADS) void pld_scan(const int32_t *const *histories,
+                                                    const int32_t *lengths, int32_t batch,
+                                                    int32_t max_len, int32_t n_min, int32_t n_max,
+                                                    DraftArgs args)
 {
+    DraftArgs a = args;
+    a.histories = histories;
+    a.lengths = lengths;
+    a.batch = batch;
+    a.max_len = max_len;
+    a.n_min = n_min;
+    a.n_max = n_max;
     static_assert(THREADS % kWave == 0, "whole wavefronts");
     static_assert(TILE % (4 * THREADS) == 0, "whole chunks per lane");
     constexpr int kWaves = THREADS / kWave;
@@ -532,7 +545,8 @@ template <int TILE, int THREADS>
 hipError_t launch_scan(const DraftArgs &a, int64_t tiles_per_req, hipStream_t s)
 {
     const int64_t grid = tiles_per_req * a.batch;
-    hipLaunchKernelGGL((pld_scan<TILE, THREADS>), dim3((unsigned)grid), dim3(THREADS), 0, s, a);
+    hipLaunchKernelGGL((pld_scan<TILE, THREADS>), dim3((unsigned)grid), dim3(THREADS), 0, s,
+                       a.histories, a.lengths, a.batch, a.max_len, a.n_min, a.n_max, a);
     return hipGetLastError();
 }
 
@@ -543,11 +557,13 @@ hipError_t launch_draft(const DraftArgs &a, int tile_tokens, hipStream_t s)
     const int64_t tiles = a.max_len > 1 ? ((int64_t)a.max_len - 1 + tile_tokens - 1) / tile_tokens : 1;
     hipError_t e;
     switch (tile_tokens) {
+    // every size keeps 4 chunks (16 tokens) per lane, except the smallest
     case 256: e = launch_scan<256, 64>(a, tiles, s); break;
-    case 1024: e = launch_scan<1024, 256>(a, tiles, s); break;
-    case 2048: e = launch_scan<2048, 256>(a, tiles, s); break;
+    case 1024: e = launch_scan<1024, 64>(a, tiles, s); break;
+    case 2048: e = launch_scan<2048, 128>(a, tiles, s); break;
     case 4096: e = launch_scan<4096, 256>(a, tiles, s); break;
-    case 8192: e = launch_scan<8192, 256>(a, tiles, s); break;
+    case 8192: e = launch_scan<8192, 512>(a, tiles, s); break;
+    case 16384: e = launch_scan<16384, 1024>(a, tiles, s); break;
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess || a.fused)

@@ -17,7 +17,7 @@ from prompt_lookup_gram_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-TILES = (256, 1024, 2048, 4096, 8192)
+TILES = (256, 1024, 2048, 4096, 8192, 16384)
 
 
 @pytest.fixture(scope="module", autouse=True)
