@@ -70,6 +70,10 @@ def parse():
     ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5],
                     help="workload: 4 (default) is the 16 x 262,144 batch; 1-3 "
                          "the smaller batches; 5 the 1,024-step streaming decode")
+    ap.add_argument("--layout", choices=["strided", "rows"], default="strided",
+                    help="histories as one padded [batch, stride] buffer per copy "
+                         "(pld_draft_batch_strided, min_len = the shortest history) "
+                         "or through a row-pointer table (pld_draft_batch)")
     ap.add_argument("--graph-steps", type=int, default=128,
                     help="draft calls captured per HIP graph")
     ap.add_argument("--latency-calls", type=int, default=2000)
@@ -120,22 +124,32 @@ def main():
 
     w = wl.ALL_CONFIGS[args.config]()
     bytes_step = 4 * w.total_tokens
-    base = B.DeviceBatch(w.histories, device=dev)
     # enough copies to defeat the Infinity Cache, capped for the tiny batches
     # (which are launch-latency bound either way)
     rot = min(64, max(1, -(-2 * MALL_BYTES // bytes_step)))
-    copies = [base] + [base.replicate() for _ in range(rot - 1)]
-    # the row-pointer tables of all copies share one small allocation, as a
-    # serving loop's per-request metadata would; only the histories rotate
-    rows_all = torch.stack([c.rows for c in copies]).contiguous()
-    ctx = B.pld_create(w.batch, base.max_len)
-    B.pld_configure(ctx, args.tile, args.fused)
     out = B.alloc_outputs(w.batch, w.k_max, device=dev)
+    if args.layout == "strided":
+        sb = B.StridedBatch(w.histories, device=dev)
+        bufs = [sb.buf] + [sb.buf.clone() for _ in range(rot - 1)]
+        ctx = B.pld_create(w.batch, sb.max_len)
 
-    def call(i, stream=None):
-        r = i % rot
-        B.pld_draft_batch(ctx, rows_all[r], copies[r].lengths, w.batch, w.n_min,
-                          w.n_max, w.k_max, out[0], out[1], out[2], stream=stream)
+        def call(i, stream=None):
+            B.pld_draft_batch_strided(ctx, bufs[i % rot], sb.stride, sb.lengths, sb.min_len,
+                                      w.batch, w.n_min, w.n_max, w.k_max, out[0], out[1],
+                                      out[2], stream=stream)
+    else:
+        base = B.DeviceBatch(w.histories, device=dev)
+        copies = [base] + [base.replicate() for _ in range(rot - 1)]
+        # the row-pointer tables of all copies share one small allocation, as
+        # a serving loop's per-request metadata would; only the histories rotate
+        rows_all = torch.stack([c.rows for c in copies]).contiguous()
+        ctx = B.pld_create(w.batch, base.max_len)
+
+        def call(i, stream=None):
+            r = i % rot
+            B.pld_draft_batch(ctx, rows_all[r], copies[r].lengths, w.batch, w.n_min,
+                              w.n_max, w.k_max, out[0], out[1], out[2], stream=stream)
+    B.pld_configure(ctx, args.tile, args.fused)
 
     # reference output (eager) for the graph check and the parity check
     call(0)
@@ -226,7 +240,8 @@ def main():
 
     graph_us = gpu_ms * 1e3 / steps           # mean launch time (one kernel per step)
     scan_gbps = bytes_step / (graph_us * 1e-6) / 1e9
-    default_launch = args.tile in (0, 4096) and args.fused in (-1, 1) and args.config == 4
+    default_launch = (args.tile in (0, 4096) and args.fused in (-1, 1) and args.config == 4
+                      and args.layout == "strided")
     traffic = profiled_traffic() if default_launch else None
     rec = {
         "metric": METRIC,
@@ -241,7 +256,7 @@ def main():
         "vs_baseline": None,
         "dtype": "int32",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch,
+        "config": {"workload": w.name, "batch": w.batch, "layout": args.layout,
                    "history_tokens": int(w.lengths.max()),
                    "n_min": w.n_min, "n_max": w.n_max, "k_max": w.k_max,
                    "bytes_per_step": bytes_step, "rotated_copies": rot,

@@ -162,10 +162,35 @@ pld_status pld_draft_batch_pos(pld_ctx *ctx, const int32_t *const *histories,
                                hipStream_t stream);
 
 /*
+ * pld_draft_batch for histories laid out at a fixed stride: row b starts at
+ * base + b * stride (a padded [batch, stride] int32 buffer, such as the
+ * context's own store). Tiles that lie inside every row by the caller's
+ * bound min_len start reading before their row's length is known, which
+ * shortens the call; pass min_len = 0 when no bound is known.
+ *
+ *  base:     device int32, 16-byte aligned.
+ *  stride:   tokens between row starts, a multiple of 4, >= 4.
+ *  lengths:  device int32[batch], min_len <= lengths[b] <= min(max_len, stride).
+ *  min_len:  0 <= min_len <= min(max_len, stride).
+ *  out_pos:  device int32[batch] or NULL (as in pld_draft_batch_pos).
+ *  Other arguments as in pld_draft_batch. A request whose length is outside
+ *  [min_len, min(max_len, stride)] is written as no match and sets the
+ *  sticky flag (PLD_EINVAL below min_len, PLD_ECAPACITY above). Only bytes
+ *  inside rows' [0, stride) spans are read.
+ * Errors: PLD_EINVAL, PLD_EHIP.
+ */
+pld_status pld_draft_batch_strided(pld_ctx *ctx, const int32_t *base, int64_t stride,
+                                   const int32_t *lengths, int32_t min_len, int32_t batch,
+                                   int32_t n_min, int32_t n_max, int32_t k_max,
+                                   int32_t *out_draft, int32_t *out_len, int32_t *out_match,
+                                   int32_t *out_pos, hipStream_t stream);
+
+/*
  * Wait for the stream, then report and clear the sticky device-side flag:
- * PLD_OK when clear; PLD_ECAPACITY when a history exceeded max_len or an
- * append overflowed; PLD_EINVAL when a length or count was negative or a
- * row pointer was null or misaligned (capacity wins when both are set).
+ * PLD_OK when clear; PLD_ECAPACITY when a history exceeded max_len (or its
+ * row's stride) or an append overflowed; PLD_EINVAL when a length or count
+ * was negative, a length was below a strided call's min_len, or a row
+ * pointer was null or misaligned (capacity wins when both are set).
  * Errors: PLD_EINVAL (null ctx), PLD_EHIP.
  */
 pld_status pld_sync(pld_ctx *ctx, hipStream_t stream);

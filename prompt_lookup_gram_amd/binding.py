@@ -27,7 +27,8 @@ PLD_N_MAX_LIMIT = 64
 # every symbol include/pld.h declares
 EXPORTS = ("pld_create", "pld_destroy", "pld_configure", "pld_append",
            "pld_store_views", "pld_store_reset", "pld_draft_batch",
-           "pld_draft_batch_pos", "pld_sync", "pld_strerror", "pld_last_error")
+           "pld_draft_batch_pos", "pld_draft_batch_strided", "pld_sync",
+           "pld_strerror", "pld_last_error")
 
 _lib = None
 
@@ -57,6 +58,8 @@ def load(path: str = LIB_PATH):
         "pld_store_reset": [vp, vp],
         "pld_draft_batch": [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp],
         "pld_draft_batch_pos": [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp],
+        "pld_draft_batch_strided": [vp, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp,
+                                    vp, vp],
         "pld_sync": [vp, vp],
     }
     for name, args in sig.items():
@@ -188,6 +191,21 @@ def pld_draft_batch_pos(ctx: int, histories, lengths, batch: int, n_min: int,
         _dev_ptr(out_pos, "out_pos", i32), _stream(stream)))
 
 
+def pld_draft_batch_strided(ctx: int, base, stride: int, lengths, min_len: int,
+                            batch: int, n_min: int, n_max: int, k_max: int, out_draft,
+                            out_len, out_match, out_pos=None, stream=None) -> None:
+    """Rows at a fixed stride: row b is base + b * stride tokens. `base` is a
+    device int32 tensor (its first element is row 0's first token) or a
+    pointer."""
+    i32 = _i32()
+    _check("pld_draft_batch_strided", load().pld_draft_batch_strided(
+        ctx, _dev_ptr(base, "base", i32), int(stride), _dev_ptr(lengths, "lengths", i32),
+        int(min_len), int(batch), int(n_min), int(n_max), int(k_max),
+        _dev_ptr(out_draft, "out_draft", i32), _dev_ptr(out_len, "out_len", i32),
+        _dev_ptr(out_match, "out_match", i32), _dev_ptr(out_pos, "out_pos", i32),
+        _stream(stream)))
+
+
 def pld_sync(ctx: int, stream=None) -> int:
     """Wait for the stream; return (and clear) the sticky device status."""
     return int(load().pld_sync(ctx, _stream(stream)))
@@ -239,6 +257,25 @@ class DeviceBatch:
         other.starts = self.starts
         other.max_len = self.max_len
         return other
+
+
+class StridedBatch:
+    """Histories in one padded [batch, stride] device buffer (stride rounded
+    up to a multiple of `align` tokens), with a lengths vector."""
+
+    def __init__(self, histories, device="cuda", align: int = 64, stride=None):
+        import torch
+        self.batch = len(histories)
+        lens = np.array([len(h) for h in histories], dtype=np.int64)
+        need = int(lens.max(initial=0))
+        self.stride = int(stride) if stride is not None else max(align, -(-need // align) * align)
+        buf = np.zeros((max(1, self.batch), self.stride), dtype=np.int32)
+        for b, h in enumerate(histories):
+            buf[b, :len(h)] = h
+        self.buf = torch.from_numpy(buf).to(device)
+        self.lengths = torch.from_numpy(lens.astype(np.int32)).to(device)
+        self.min_len = int(lens.min(initial=0))
+        self.max_len = max(1, need)
 
 
 def alloc_outputs(batch: int, k_max: int, device="cuda"):

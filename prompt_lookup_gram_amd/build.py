@@ -21,7 +21,7 @@ ARCH = "gfx950"
 # Packed-FP32 instruction selection is switched off for all device code.
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
              # the scan's leading kernel arguments arrive in SGPRs
-             "-mllvm", "-amdgpu-kernarg-preload-count=6",
+             "-mllvm", "-amdgpu-kernarg-preload-count=8",
              "-Wall", "-Wextra", "-Werror", "-Wno-unused-command-line-argument",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I", INCLUDE, "-I", CSRC]

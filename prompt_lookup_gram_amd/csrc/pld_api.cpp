@@ -83,6 +83,9 @@ pld_status check_draft_args(pld_ctx *ctx, const int32_t *const *histories,
         return fail(PLD_EINVAL, "batch %d outside [0, max_batch=%d]", batch, ctx->max_batch);
     if (batch > 0 && (!histories || !lengths || !out_draft || !out_len || !out_match))
         return fail(PLD_EINVAL, "null buffer pointer");
+    if (batch > 0 && (((uintptr_t)lengths | (uintptr_t)out_draft | (uintptr_t)out_len |
+                       (uintptr_t)out_match) & 3u))
+        return fail(PLD_EINVAL, "lengths and outputs must be 4-byte aligned");
     if ((int64_t)batch * k_max > INT64_MAX / 4)
         return fail(PLD_EINVAL, "batch * k_max too large");
     if (pld::scan_grid(ctx->max_len, batch, ctx->tile_tokens) > 0x7fffffffLL)
@@ -91,19 +94,36 @@ pld_status check_draft_args(pld_ctx *ctx, const int32_t *const *histories,
     return PLD_OK;
 }
 
-pld_status draft(pld_ctx *ctx, const int32_t *const *histories, const int32_t *lengths,
+pld_status draft(pld_ctx *ctx, const int32_t *const *histories, const int32_t *base,
+                 int64_t stride, int32_t min_len, const int32_t *lengths,
                  int32_t batch, int32_t n_min, int32_t n_max, int32_t k_max,
                  int32_t *out_draft, int32_t *out_len, int32_t *out_match,
                  int32_t *out_pos, hipStream_t stream)
 {
-    pld_status s = check_draft_args(ctx, histories, lengths, batch, n_min, n_max, k_max,
+    // a strided batch stands in for the row table in the common checks
+    const int32_t *const *rows_or_base =
+        stride ? (const int32_t *const *)(const void *)base : histories;
+    pld_status s = check_draft_args(ctx, rows_or_base, lengths, batch, n_min, n_max, k_max,
                                     out_draft, out_len, out_match);
     if (s != PLD_OK)
         return s;
+    if (stride) {
+        if ((uintptr_t)base & 15u)
+            return fail(PLD_EINVAL, "strided batch: base must be 16-byte aligned");
+        if (stride < 4 || (stride & 3))
+            return fail(PLD_EINVAL, "strided batch: stride must be a positive multiple of 4 "
+                        "tokens (got %lld)", (long long)stride);
+        if (min_len < 0 || min_len > ctx->max_len || min_len > stride)
+            return fail(PLD_EINVAL, "strided batch: min_len %d outside [0, min(max_len, stride)]",
+                        min_len);
+    }
     if (batch == 0)
         return PLD_OK;
     pld::DraftArgs a;
     a.histories = histories;
+    a.base = base;
+    a.stride = stride;
+    a.min_len = min_len;
     a.lengths = lengths;
     a.batch = batch;
     a.n_min = n_min;
@@ -282,8 +302,8 @@ pld_status pld_draft_batch(pld_ctx *ctx, const int32_t *const *histories,
                            int32_t n_max, int32_t k_max, int32_t *out_draft,
                            int32_t *out_len, int32_t *out_match, hipStream_t stream)
 {
-    return draft(ctx, histories, lengths, batch, n_min, n_max, k_max, out_draft, out_len,
-                 out_match, nullptr, stream);
+    return draft(ctx, histories, nullptr, 0, 0, lengths, batch, n_min, n_max, k_max, out_draft,
+                 out_len, out_match, nullptr, stream);
 }
 
 pld_status pld_draft_batch_pos(pld_ctx *ctx, const int32_t *const *histories,
@@ -294,8 +314,21 @@ pld_status pld_draft_batch_pos(pld_ctx *ctx, const int32_t *const *histories,
 {
     if (batch > 0 && !out_pos)
         return fail(PLD_EINVAL, "out_pos is null");
-    return draft(ctx, histories, lengths, batch, n_min, n_max, k_max, out_draft, out_len,
-                 out_match, out_pos, stream);
+    return draft(ctx, histories, nullptr, 0, 0, lengths, batch, n_min, n_max, k_max, out_draft,
+                 out_len, out_match, out_pos, stream);
+}
+
+pld_status pld_draft_batch_strided(pld_ctx *ctx, const int32_t *base, int64_t stride,
+                                   const int32_t *lengths, int32_t min_len, int32_t batch,
+                                   int32_t n_min, int32_t n_max, int32_t k_max,
+                                   int32_t *out_draft, int32_t *out_len, int32_t *out_match,
+                                   int32_t *out_pos, hipStream_t stream)
+{
+    if (stride <= 0)
+        return fail(PLD_EINVAL, "strided batch: stride must be positive (got %lld)",
+                    (long long)stride);
+    return draft(ctx, nullptr, base, stride, min_len, lengths, batch, n_min, n_max, k_max,
+                 out_draft, out_len, out_match, out_pos, stream);
 }
 
 pld_status pld_sync(pld_ctx *ctx, hipStream_t stream)
@@ -317,10 +350,11 @@ pld_status pld_sync(pld_ctx *ctx, hipStream_t stream)
                     (bits & pld::kErrLenCapacity) ? "a history longer than max_len " : "",
                     (bits & pld::kErrAppendCapacity) ? "an append past max_len" : "");
     if (bits)
-        return fail(PLD_EINVAL, "device reported: %s%s%s",
+        return fail(PLD_EINVAL, "device reported: %s%s%s%s",
                     (bits & pld::kErrLenNegative) ? "a negative length " : "",
                     (bits & pld::kErrBadRow) ? "a null or misaligned row pointer " : "",
-                    (bits & pld::kErrAppendNegative) ? "a negative append count" : "");
+                    (bits & pld::kErrAppendNegative) ? "a negative append count " : "",
+                    (bits & pld::kErrBelowMinLen) ? "a length below the promised min_len" : "");
     return PLD_OK;
 }
 

@@ -18,7 +18,8 @@ enum : uint32_t {
     kErrLenNegative = 2u,     // lengths[b] < 0
     kErrBadRow = 4u,          // null or misaligned row pointer with L > 0
     kErrAppendCapacity = 8u,  // append would pass max_len
-    kErrAppendNegative = 16u  // counts[b] < 0
+    kErrAppendNegative = 16u, // counts[b] < 0
+    kErrBelowMinLen = 32u     // strided batch: lengths[b] < the caller's min_len
 };
 
 // Per-request reduction state: the packed key maximum and the arrival
@@ -31,7 +32,10 @@ struct alignas(256) ReqSlot {
 };
 
 struct DraftArgs {
-    const int32_t *const *histories;
+    const int32_t *const *histories;  // row table (stride == 0)
+    const int32_t *base;              // strided batch: row b at base + b * stride
+    int64_t stride;                   // tokens between rows; 0 for a row table
+    int32_t min_len;                  // strided batch: lower bound on every length
     const int32_t *lengths;
     int32_t batch;
     int32_t n_min, n_max, k_max;

@@ -125,17 +125,21 @@ struct Req {
     uint32_t err;   // error bits for this request
 };
 
+// Row b is histories[b], or base + b * stride for a strided batch (a.stride
+// > 0, rows 16-byte aligned as checked on the host).
 __device__ __forceinline__ Req load_req(const DraftArgs &a, int b, int tile_tokens)
 {
     Req r;
     const int32_t len = a.lengths[b];
-    const int32_t *h = a.histories[b];
+    const int32_t *h = a.stride ? a.base + (int64_t)b * a.stride : a.histories[b];
     r.err = 0;
     if (len < 0)
         r.err |= kErrLenNegative;
-    else if (len > a.max_len)
+    else if (len > a.max_len || (a.stride && len > a.stride))
         r.err |= kErrLenCapacity;
-    else if (len > 0 && (h == nullptr || ((uintptr_t)h & 3u)))
+    else if (a.stride && len < a.min_len)
+        r.err |= kErrBelowMinLen;
+    else if (!a.stride && len > 0 && (h == nullptr || ((uintptr_t)h & 3u)))
         r.err |= kErrBadRow;
     r.h = h;
     r.L = r.err ? 0 : len;
@@ -215,13 +219,45 @@ __device__ __forceinline__ void wait_vm()
 // from LDS up to m tokens.
 // CHECKED (the first and last tile of a request): loads stay inside the row
 // and every position is range-checked; interior tiles skip both.
-template <int TILE, int THREADS, bool CHECKED, bool FILTER3>
+template <int TILE, int THREADS>
+struct WaveGeom {
+    static constexpr int kWaves = THREADS / kWave;
+    static constexpr int kSpan = TILE / 4 / kWaves;  // chunks per wavefront
+    static constexpr int kPer = kSpan / kWave;       // chunks per lane
+};
+
+// Issues this lane's loads of an interior tile (no range checks): its kPer
+// span chunks and the extra chunk (halo for lanes 0..15, the chunk after the
+// span for lane 16; other lanes re-read their first chunk). With `real`
+// false every lane reads the context's 16 zero bytes instead (a load with
+// no branch around it that moves no data worth counting).
+template <int TILE, int THREADS>
+__device__ __forceinline__ void load_interior(const int4 *arow, int64_t t0, bool real,
+                                              const int4 *zero16,
+                                              int4 (&v)[WaveGeom<TILE, THREADS>::kPer + 1])
+{
+    constexpr int kSpan = WaveGeom<TILE, THREADS>::kSpan;
+    constexpr int kPer = WaveGeom<TILE, THREADS>::kPer;
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t gq0 = (t0 - kHalo) / 4 + (int64_t)wave * kSpan;  // exact
+    const int qx = lane < kHaloChunks ? lane : (lane == kHaloChunks ? kHaloChunks + kSpan : -1);
+    // the extra chunk first: slot 0's tests need the halo
+    v[kPer] = gld_stream(real ? arow + (gq0 + (qx >= 0 ? qx : kHaloChunks + lane)) : zero16);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        v[k] = gld_stream(real ? arow + (gq0 + kHaloChunks + k * kWave + lane) : zero16);
+}
+
+template <int TILE, int THREADS, bool CHECKED, bool FILTER3, bool PRELOADED>
 __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64_t t0,
-                                         int32_t mhat, int4 *lds_win, int32_t *lds_pat)
+                                         int32_t mhat, int4 *lds_win, int32_t *lds_pat,
+                                         int4 (&v)[WaveGeom<TILE, THREADS>::kPer + 1])
 {
     constexpr int kWaves = THREADS / kWave;
     constexpr int kSpan = TILE / 4 / kWaves;         // chunks per wavefront
     constexpr int kPer = kSpan / kWave;              // chunks per lane
+    static_assert(!(PRELOADED && CHECKED), "only interior tiles are loaded ahead");
     constexpr int kWinW = kHaloChunks + kSpan + 1;   // per-wavefront window
     static_assert(kSpan % kWave == 0, "whole chunks per lane");
 
@@ -251,13 +287,10 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
     const int32_t p2 = gld(r.h + r.L - 2);  // L >= 2 whenever a tile is scanned
     const int32_t p3 = gld(r.h + r.L - (mhat >= 3 ? 3 : 1));
     const int32_t pv = gld(r.h + r.L - mhat + (lane < mhat ? lane : 0));
-    int4 v[kPer + 1];
-    if constexpr (!CHECKED) {
-        // the extra chunk first: slot 0's tests need the halo
-        v[kPer] = gld_stream(arow + (gq0 + (qx >= 0 ? qx : kHaloChunks + lane)));
-#pragma unroll
-        for (int k = 0; k < kPer; ++k)
-            v[k] = gld_stream(arow + (gq0 + kHaloChunks + k * kWave + lane));
+    if constexpr (PRELOADED) {
+        // the caller issued this tile's loads before the length was known
+    } else if constexpr (!CHECKED) {
+        load_interior<TILE, THREADS>(arow, t0, true, a.zero16, v);
     } else {
         bool inside[kPer + 1];
 #pragma unroll
@@ -387,16 +420,28 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
 }
 
 // The fields needed first are separate leading arguments so that they can be
-// preloaded into SGPRs at wave launch (no scalar load of the kernel
-// arguments before the row table can be read); the rest come in `args`.
-template <int TILE, int THREADS>
-__global__ __launch_bounds__(THREADS) void pld_scan(const int32_t *const *histories,
-                                                    const int32_t *lengths, int32_t batch,
-                                                    int32_t max_len, int32_t n_min, int32_t n_max,
-                                                    DraftArgs args)
+// preloaded into SGPRs at wave launch; the rest come in `args`.
+//
+// STRIDED batches (row b at base + b * stride) know every tile's address
+// from those arguments alone. A tile that lies inside every row by the
+// caller's bound min_len (checked against each length on the device) then
+// issues its loads at once, before its length is read from memory; other
+// tiles, and row-table batches, read the length and row first.
+template <int TILE, int THREADS, bool STRIDED>
+__global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int32_t *lengths,
+                                                    int32_t batch, int32_t max_len,
+                                                    int32_t n_min, int32_t n_max, int64_t stride,
+                                                    int32_t min_len, DraftArgs args)
 {
     DraftArgs a = args;
-    a.histories = histories;
+    if constexpr (STRIDED) {
+        a.base = (const int32_t *)rows;
+        a.stride = stride;
+        a.min_len = min_len;
+    } else {
+        a.histories = (const int32_t *const *)rows;
+        a.stride = 0;
+    }
     a.lengths = lengths;
     a.batch = batch;
     a.max_len = max_len;
@@ -406,6 +451,7 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const int32_t *const *histor
     static_assert(TILE % (4 * THREADS) == 0, "whole chunks per lane");
     constexpr int kWaves = THREADS / kWave;
     constexpr int kWinW = kHaloChunks + TILE / 4 / kWaves + 1;
+    constexpr int kPer = WaveGeom<TILE, THREADS>::kPer;
     static_assert(kWave >= PLD_N_MAX_LIMIT, "one suffix token per lane");
 
     __shared__ int4 win[kWaves * kWinW];
@@ -416,6 +462,17 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const int32_t *const *histor
     const int tid = threadIdx.x;
     const int tile = blockIdx.x / a.batch;
     const int b = blockIdx.x - tile * a.batch;
+    const int64_t t0 = (int64_t)tile * TILE;
+
+    int4 v[kPer + 1];
+    bool ahead = false;
+    if constexpr (STRIDED) {
+        // interior for every row of length >= min_len
+        ahead = t0 >= kHalo + 4 && t0 + TILE + 4 <= (int64_t)min_len - 1;
+        const int4 *arow = (const int4 *)(a.base + (int64_t)b * stride);
+        // a tile not loaded ahead re-reads the row's first chunk in every lane
+        load_interior<TILE, THREADS>(arow, t0, ahead, arow, v);
+    }
 
     const Req r = load_req(a, b, TILE);
     if (tile >= r.ntiles)
@@ -426,17 +483,19 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const int32_t *const *histor
     const int32_t mhat = r.L - 1 < a.n_max ? r.L - 1 : a.n_max;
     u64 best = 0;
     if (mhat >= a.n_min) {
-        const int64_t t0 = (int64_t)tile * TILE;
         // interior: halo and the chunk after the tile lie inside the row and
         // every position of the tile is a candidate
         const bool interior = t0 >= kHalo + 4 && t0 + TILE + 4 <= (int64_t)r.L - 1;
         const bool f3 = a.n_min >= 3;
-        if (interior)
-            best = f3 ? scan_wave<TILE, THREADS, false, true>(a, r, t0, mhat, win, pat)
-                      : scan_wave<TILE, THREADS, false, false>(a, r, t0, mhat, win, pat);
+        if (STRIDED && ahead && r.err == 0)
+            best = f3 ? scan_wave<TILE, THREADS, false, true, true>(a, r, t0, mhat, win, pat, v)
+                      : scan_wave<TILE, THREADS, false, false, true>(a, r, t0, mhat, win, pat, v);
+        else if (interior)
+            best = f3 ? scan_wave<TILE, THREADS, false, true, false>(a, r, t0, mhat, win, pat, v)
+                      : scan_wave<TILE, THREADS, false, false, false>(a, r, t0, mhat, win, pat, v);
         else
-            best = f3 ? scan_wave<TILE, THREADS, true, true>(a, r, t0, mhat, win, pat)
-                      : scan_wave<TILE, THREADS, true, false>(a, r, t0, mhat, win, pat);
+            best = f3 ? scan_wave<TILE, THREADS, true, true, false>(a, r, t0, mhat, win, pat, v)
+                      : scan_wave<TILE, THREADS, true, false, false>(a, r, t0, mhat, win, pat, v);
     }
 
     // 5. wavefront maximum by DPP (only in wavefronts that found a match),
@@ -545,8 +604,14 @@ template <int TILE, int THREADS>
 hipError_t launch_scan(const DraftArgs &a, int64_t tiles_per_req, hipStream_t s)
 {
     const int64_t grid = tiles_per_req * a.batch;
-    hipLaunchKernelGGL((pld_scan<TILE, THREADS>), dim3((unsigned)grid), dim3(THREADS), 0, s,
-                       a.histories, a.lengths, a.batch, a.max_len, a.n_min, a.n_max, a);
+    if (a.stride)
+        hipLaunchKernelGGL((pld_scan<TILE, THREADS, true>), dim3((unsigned)grid), dim3(THREADS), 0,
+                           s, (const void *)a.base, a.lengths, a.batch, a.max_len, a.n_min,
+                           a.n_max, a.stride, a.min_len, a);
+    else
+        hipLaunchKernelGGL((pld_scan<TILE, THREADS, false>), dim3((unsigned)grid), dim3(THREADS), 0,
+                           s, (const void *)a.histories, a.lengths, a.batch, a.max_len, a.n_min,
+                           a.n_max, (int64_t)0, 0, a);
     return hipGetLastError();
 }
 

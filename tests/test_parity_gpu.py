@@ -395,3 +395,122 @@ def test_append_overflow_sets_capacity_flag():
         assert got.tolist() == [0, 0]
     finally:
         B.pld_destroy(ctx)
+
+
+# ---------------------------------------------------------------------------
+# strided batches (rows at a fixed stride, tiles read ahead of the lengths)
+# ---------------------------------------------------------------------------
+
+
+def run_strided(w, min_len, tile=0, fused=-1, stride=None, max_len=None):
+    sb = B.StridedBatch(w.histories, stride=stride)
+    ctx = B.pld_create(max(1, w.batch), max_len or max(sb.max_len, min_len, 1))
+    try:
+        B.pld_configure(ctx, tile, fused)
+        out = B.alloc_outputs(w.batch, w.k_max)
+        for t in out:
+            t.fill_(-7)
+        B.pld_draft_batch_strided(ctx, sb.buf, sb.stride, sb.lengths, min_len, w.batch,
+                                  w.n_min, w.n_max, w.k_max, *out)
+        st = B.pld_sync(ctx)
+    finally:
+        B.pld_destroy(ctx)
+    return st, [t.cpu().numpy() for t in out]
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+@pytest.mark.parametrize("bound", ["exact", "zero", "half"])
+def test_strided_config_parity(cfg, bound):
+    w = wl.ALL_CONFIGS[cfg]()
+    lmin = int(w.lengths.min())
+    min_len = {"exact": lmin, "zero": 0, "half": lmin // 2}[bound]
+    st, got = run_strided(w, min_len)
+    assert st == B.PLD_OK
+    assert_parity(w, got, f"strided min_len={min_len}")
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("fused", [1, 0])
+def test_strided_every_tiling(cfg, tile, fused):
+    w = wl.ALL_CONFIGS[cfg]()
+    st, got = run_strided(w, int(w.lengths.min()), tile=tile, fused=fused)
+    assert st == B.PLD_OK
+    assert_parity(w, got, f"strided tile={tile} fused={fused}")
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_strided_fuzz(seed):
+    w = wl.fuzz_batch(seed)
+    rng = np.random.default_rng([321, seed])
+    lmin = int(w.lengths.min())
+    min_len = int(rng.integers(0, lmin + 1))
+    extra = int(rng.integers(0, 3)) * 4
+    stride = max(4, -(-max(1, w.max_len) // 4) * 4 + extra)
+    st, got = run_strided(w, min_len, tile=int(rng.choice(TILES)),
+                          fused=int(rng.integers(0, 2)), stride=stride)
+    assert st == B.PLD_OK
+    assert_parity(w, got, f"strided min_len={min_len} stride={stride}")
+
+
+def test_strided_store_views_match_row_table():
+    """The context's own store drafted through its row table and through a
+    strided call over the same memory give the same outputs."""
+    import torch
+    start = wl.config5_start()
+    nb = 8
+    ctx = B.pld_create(nb, wl.STREAM_MAX_LEN, own_store=True)
+    try:
+        rows, lens = B.pld_store_views(ctx)
+        init = torch.from_numpy(np.stack(start.histories[:nb])).cuda()
+        B.pld_append(ctx, init, wl.STREAM_START_LEN,
+                     torch.full((nb,), wl.STREAM_START_LEN, dtype=torch.int32,
+                                device="cuda"), nb)
+        table = np.zeros(nb, np.int64)
+        _hip_copy_to_host(table, rows)
+        pitch = int((table[1] - table[0]) // 4)
+        a = B.alloc_outputs(nb, 16)
+        b_ = B.alloc_outputs(nb, 16)
+        B.pld_draft_batch_pos(ctx, rows, lens, nb, 4, 12, 16, *a)
+        B.pld_draft_batch_strided(ctx, int(table[0]), pitch, lens, wl.STREAM_START_LEN,
+                                  nb, 4, 12, 16, *b_)
+        assert B.pld_sync(ctx) == B.PLD_OK
+        for x, y in zip(a, b_):
+            assert torch.equal(x, y)
+    finally:
+        B.pld_destroy(ctx)
+
+
+def test_strided_errors():
+    import torch
+    rng = np.random.default_rng(9)
+    hs = [rng.integers(0, 3, 600).astype(np.int32) for _ in range(3)]
+    sb = B.StridedBatch(hs)
+    ctx = B.pld_create(3, 1000)
+    out = B.alloc_outputs(3, 5)
+    try:
+        # host-side: misaligned base, bad stride, min_len out of range
+        with pytest.raises(B.PldError):
+            B.pld_draft_batch_strided(ctx, sb.buf.data_ptr() + 4, sb.stride, sb.lengths,
+                                      0, 3, 2, 8, 5, *out)
+        with pytest.raises(B.PldError):
+            B.pld_draft_batch_strided(ctx, sb.buf, 6, sb.lengths, 0, 3, 2, 8, 5, *out)
+        with pytest.raises(B.PldError):
+            B.pld_draft_batch_strided(ctx, sb.buf, sb.stride, sb.lengths, sb.stride + 4,
+                                      3, 2, 8, 5, *out)
+        # device-side: a length below min_len, and one above the stride
+        od, ol, om, oj = oracle.draft(hs, 2, 8, 5)
+        L = sb.lengths.clone(); L[1] = 100
+        B.pld_draft_batch_strided(ctx, sb.buf, sb.stride, L, 500, 3, 2, 8, 5, *out)
+        assert B.pld_sync(ctx) == B.PLD_EINVAL
+        d, l, m, p = [t.cpu().numpy() for t in out]
+        assert m[1] == 0 and np.all(d[1] == -1)
+        for b in (0, 2):
+            assert (m[b], p[b], l[b]) == (om[b], oj[b], ol[b]) and np.array_equal(d[b], od[b])
+        L = sb.lengths.clone(); L[2] = sb.stride + 1
+        B.pld_draft_batch_strided(ctx, sb.buf, sb.stride, L, 0, 3, 2, 8, 5, *out)
+        assert B.pld_sync(ctx) == B.PLD_ECAPACITY
+        assert B.pld_sync(ctx) == B.PLD_OK
+    finally:
+        B.pld_destroy(ctx)
+    del torch
