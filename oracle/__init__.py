@@ -4,10 +4,12 @@ TEST INFRASTRUCTURE ONLY: only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package. The product library
 (``prompt_lookup_gram_amd``) never imports it.
 
-The arithmetic lives in ``pld_oracle.c`` (plain, single-threaded C, compiled
-with gcc at -O2 without vector intrinsics); this wrapper only marshals numpy
-arrays. The rule it implements is stated at the top of that file (HyperQwen
-lookup-drafting page, step 1 of the three-step principle).
+The arithmetic lives in ``pld_oracle.c`` (lookup drafting: HyperQwen
+lookup-drafting page, step 1 of the three-step principle) and
+``fuse_oracle.c`` (draft fusion and long-block scheduling: steps 2 and 3 of
+the same page), plain single-threaded C compiled with gcc at -O2 without
+vector intrinsics; this wrapper only marshals numpy arrays. The rules are
+stated at the top of each file.
 """
 
 from __future__ import annotations
@@ -19,17 +21,24 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "pld_oracle.c")
+_SRCS = [os.path.join(_HERE, "pld_oracle.c"), os.path.join(_HERE, "fuse_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "libpld_oracle.so")
 _lib = None
 
 
+def compile_lib(out_path: str, sources=None) -> str:
+    """Compile the oracle sources (default: this package's) into a shared
+    library at out_path with gcc."""
+    subprocess.run(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror",
+                    "-fPIC", "-shared", "-o", out_path, *(sources or _SRCS)], check=True)
+    return out_path
+
+
 def build(force: bool = True) -> str:
-    """Compile pld_oracle.c into libpld_oracle.so with gcc."""
+    """Compile the oracle sources into libpld_oracle.so with gcc."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + f".tmp{os.getpid()}"
-        subprocess.run(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror",
-                        "-fPIC", "-shared", "-o", tmp, _SRC], check=True)
+        compile_lib(tmp)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -58,11 +67,38 @@ def _bind(lib):
                                            ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_int32, i32p,
                                            i32p, i32p, i64p]
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    lib.fuse_oracle_batch.restype = ctypes.c_int
+    lib.fuse_oracle_batch.argtypes = [ctypes.POINTER(FuseParams), ctypes.c_int32, i32p,
+                                      ctypes.c_int32, i32p, i32p, i32p, i32p, i32p, i32p,
+                                      i32p, u64p]
     return lib
 
 
 class OracleError(RuntimeError):
     pass
+
+
+class FuseParams(ctypes.Structure):
+    """Fusion and scheduling parameters, defaults as the HyperQwen
+    lookup-drafting page gives them (steps 2 and 3): a 7-token drafter head,
+    15 draft positions in a long block, replace at a match of 8, or of 6 when
+    the first 2 tokens agree, fill the tail at 4, two near-full steps to
+    enter, 3 sticky steps. near_full_slack 1 is a reading (the page does not
+    quantify "near-full")."""
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "head", "positions_long", "replace_min", "agree_min", "agree_tokens",
+        "tail_min", "entry_steps", "sticky", "near_full_slack")]
+
+    def __init__(self, head=7, positions_long=15, replace_min=8, agree_min=6,
+                 agree_tokens=2, tail_min=4, entry_steps=2, sticky=3, near_full_slack=1):
+        super().__init__(head, positions_long, replace_min, agree_min, agree_tokens,
+                         tail_min, entry_steps, sticky, near_full_slack)
+
+
+#: words of per-request fusion state (long flag, hold, near-full run, previous
+#: block positions); all zero before a request's first step
+FUSE_STATE_WORDS = 4
 
 
 def draft(histories, n_min: int, n_max: int, k_max: int, lib=None):
@@ -99,3 +135,34 @@ def append(histories, tokens: np.ndarray, counts: np.ndarray):
     list of histories (the inputs are not modified)."""
     return [np.concatenate([h, np.asarray(tokens[b, :int(counts[b])], dtype=np.int32)])
             for b, h in enumerate(histories)]
+
+
+def fuse(params: FuseParams, lookup, lookup_len, lookup_match, drafter, accepted,
+         state, lib=None):
+    """One fusion step for a batch (HyperQwen page, steps 2 and 3).
+
+    lookup [B, K] int32 lookup draft rows with lengths lookup_len [B] and
+    match lengths lookup_match [B]; drafter [B, head] int32; accepted [B]
+    int32 (previous step's accepted draft tokens); state [B, 4] int32.
+    Returns (block [B, positions_long], positions [B], src [B] uint64 bit
+    masks, new state [B, 4]); the inputs are not modified.
+    """
+    lib = load() if lib is None else lib
+    lookup = np.ascontiguousarray(lookup, dtype=np.int32)
+    batch, k = lookup.shape
+    drafter = np.ascontiguousarray(drafter, dtype=np.int32).reshape(batch, params.head)
+    lookup_len = np.ascontiguousarray(lookup_len, dtype=np.int32)
+    lookup_match = np.ascontiguousarray(lookup_match, dtype=np.int32)
+    accepted = np.ascontiguousarray(accepted, dtype=np.int32)
+    st = np.array(state, dtype=np.int32).reshape(batch, FUSE_STATE_WORDS).copy()
+    block = np.empty((batch, params.positions_long), dtype=np.int32)
+    positions = np.empty(batch, dtype=np.int32)
+    src = np.empty(batch, dtype=np.uint64)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    p = lambda a: a.ctypes.data_as(i32p)  # noqa: E731
+    rc = lib.fuse_oracle_batch(ctypes.byref(params), batch, p(lookup), k, p(lookup_len),
+                               p(lookup_match), p(drafter), p(accepted), p(st), p(block),
+                               p(positions), src.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)))
+    if rc != 0:
+        raise OracleError(f"fusion oracle rejected arguments (rc={rc})")
+    return block, positions, src, st
