@@ -186,11 +186,93 @@ pld_status pld_draft_batch_strided(pld_ctx *ctx, const int32_t *base, int64_t st
                                    int32_t *out_pos, hipStream_t stream);
 
 /*
+ * Draft fusion and long-block scheduling (HyperQwen lookup-drafting page,
+ * "lookup drafting: the three-step principle", steps 2 and 3).
+ *
+ * Before each verify step the lookup draft and a small drafter's proposal
+ * are merged into the block of draft positions the target model verifies:
+ *  - scheduling (step 3): a long block of positions_long draft positions runs
+ *    only while the request is copying: it starts on a step whose lookup
+ *    match is >= tail_min with a draft covering all positions_long
+ *    positions, when the entry_steps steps before it were near-full
+ *    (accepted >= their positions - near_full_slack); it is held sticky
+ *    further steps after that condition fails. Otherwise the block has the
+ *    drafter's head positions.
+ *  - fusion (step 2): head positions 0 .. head-1 hold the drafter's tokens;
+ *    the lookup draft replaces them (where it has tokens) when its match is
+ *    >= replace_min, or >= agree_min with the drafter's first agree_tokens
+ *    tokens equal to the lookup's. In a long block, tail positions
+ *    head .. positions_long-1 take the lookup's tokens when its match is
+ *    >= tail_min, up to the end of the lookup draft; the block ends at the
+ *    first tail position the lookup does not cover.
+ * Readings of points the page leaves open: near-full, the run of two, the
+ * tail test, the hold re-armed by every entry step, a partial head
+ * replacement, a gap ending the block (the same in pld_fuse's contract and
+ * the test oracle).
+ */
+typedef struct pld_fuse_params {
+    int32_t head;            /* drafter positions; the page: 7 */
+    int32_t positions_long;  /* draft positions of a long block (<= 64); 15 */
+    int32_t replace_min;     /* head: match length that replaces outright; 8 */
+    int32_t agree_min;       /* head: match length that replaces on agreement; 6 */
+    int32_t agree_tokens;    /* head: leading tokens that must agree; 2 */
+    int32_t tail_min;        /* tail: match length that fills it; 4 */
+    int32_t entry_steps;     /* near-full steps in a row before a long block; 2 */
+    int32_t sticky;          /* steps a long block is held; 3 */
+    int32_t near_full_slack; /* a near-full step misses at most this many; 1 */
+} pld_fuse_params;
+
+/* int32 words of per-request state: long flag, hold left, near-full run,
+   draft positions of the previous block. All zero before a request's first
+   step (and to restart it). */
+#define PLD_FUSE_STATE_WORDS 4
+#define PLD_FUSE_MAX_POSITIONS 64
+
+/* The page's values: 7, 15, 8, 6, 2, 4, 2, 3, and slack 1 (a reading).
+   Errors: PLD_EINVAL (null). */
+pld_status pld_fuse_params_default(pld_fuse_params *params);
+
+/*
+ * One fused step for a batch.
+ *
+ *  params:       host struct; 1 <= head <= positions_long <= 64,
+ *                1 <= agree_tokens <= head, replace_min, agree_min,
+ *                tail_min >= 1, entry_steps, sticky, near_full_slack >= 0.
+ *  lookup:       device int32[batch * lookup_k]: row b holds request b's
+ *                lookup draft (pld_draft_batch's out_draft with k_max =
+ *                lookup_k >= 1).
+ *  lookup_len, lookup_match: device int32[batch]: its draft and match
+ *                lengths (out_len, out_match).
+ *  drafter:      device int32[batch * head], the drafter's proposals.
+ *  accepted:     device int32[batch]: draft tokens the verifier accepted at
+ *                the request's previous step (read only when it had one).
+ *  state:        device int32[batch * PLD_FUSE_STATE_WORDS], read and
+ *                updated; row b belongs to request b.
+ *  out_block:    device int32[batch * positions_long]: the fused block, -1
+ *                past its draft positions.
+ *  out_positions: device int32[batch]: draft positions to verify.
+ *  out_src:      device uint64[batch] or NULL: bit t set when block
+ *                position t came from the lookup (the positions a sampler
+ *                turns into point masses on the proposed token).
+ * Device-side input errors (lookup_len outside [0, lookup_k], a negative
+ * match, accepted outside [0, previous positions], a state row no step
+ * could have written) give that request the drafter's head, reset its
+ * state to zero and set the sticky flag (PLD_EINVAL at pld_sync).
+ * Errors: PLD_EINVAL (bad params, sizes or null pointers), PLD_EHIP.
+ */
+pld_status pld_fuse(pld_ctx *ctx, const pld_fuse_params *params, const int32_t *lookup,
+                    int32_t lookup_k, const int32_t *lookup_len, const int32_t *lookup_match,
+                    const int32_t *drafter, const int32_t *accepted, int32_t *state,
+                    int32_t batch, int32_t *out_block, int32_t *out_positions,
+                    uint64_t *out_src, hipStream_t stream);
+
+/*
  * Wait for the stream, then report and clear the sticky device-side flag:
  * PLD_OK when clear; PLD_ECAPACITY when a history exceeded max_len (or its
  * row's stride) or an append overflowed; PLD_EINVAL when a length or count
- * was negative, a length was below a strided call's min_len, or a row
- * pointer was null or misaligned (capacity wins when both are set).
+ * was negative, a length was below a strided call's min_len, a row pointer
+ * was null or misaligned, or pld_fuse saw inconsistent per-request inputs
+ * (capacity wins when both are set).
  * Errors: PLD_EINVAL (null ctx), PLD_EHIP.
  */
 pld_status pld_sync(pld_ctx *ctx, hipStream_t stream);

@@ -23,14 +23,24 @@ PLD_ENOMEM = 2
 PLD_EHIP = 3
 PLD_ECAPACITY = 4
 PLD_N_MAX_LIMIT = 64
+PLD_FUSE_STATE_WORDS = 4
+PLD_FUSE_MAX_POSITIONS = 64
 
 # every symbol include/pld.h declares
 EXPORTS = ("pld_create", "pld_destroy", "pld_configure", "pld_append",
            "pld_store_views", "pld_store_reset", "pld_draft_batch",
-           "pld_draft_batch_pos", "pld_draft_batch_strided", "pld_sync",
-           "pld_strerror", "pld_last_error")
+           "pld_draft_batch_pos", "pld_draft_batch_strided", "pld_fuse_params_default",
+           "pld_fuse", "pld_sync", "pld_strerror", "pld_last_error")
 
 _lib = None
+
+
+class PldFuseParams(ctypes.Structure):
+    """pld_fuse_params (include/pld.h): fusion and long-block scheduling
+    parameters; pld_fuse_params_default() gives the HyperQwen page's values."""
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "head", "positions_long", "replace_min", "agree_min", "agree_tokens",
+        "tail_min", "entry_steps", "sticky", "near_full_slack")]
 
 
 class PldError(RuntimeError):
@@ -60,6 +70,9 @@ def load(path: str = LIB_PATH):
         "pld_draft_batch_pos": [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp],
         "pld_draft_batch_strided": [vp, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp,
                                     vp, vp],
+        "pld_fuse_params_default": [ctypes.POINTER(PldFuseParams)],
+        "pld_fuse": [vp, ctypes.POINTER(PldFuseParams), vp, i32, vp, vp, vp, vp, vp, i32,
+                     vp, vp, vp, vp],
         "pld_sync": [vp, vp],
     }
     for name, args in sig.items():
@@ -204,6 +217,29 @@ def pld_draft_batch_strided(ctx: int, base, stride: int, lengths, min_len: int,
         _dev_ptr(out_draft, "out_draft", i32), _dev_ptr(out_len, "out_len", i32),
         _dev_ptr(out_match, "out_match", i32), _dev_ptr(out_pos, "out_pos", i32),
         _stream(stream)))
+
+
+def pld_fuse_params_default() -> PldFuseParams:
+    p = PldFuseParams()
+    _check("pld_fuse_params_default", load().pld_fuse_params_default(ctypes.byref(p)))
+    return p
+
+
+def pld_fuse(ctx: int, params: PldFuseParams, lookup, lookup_k: int, lookup_len,
+             lookup_match, drafter, accepted, state, batch: int, out_block, out_positions,
+             out_src=None, stream=None) -> None:
+    """One fusion step (include/pld.h). `state` is an int32 [batch, 4] device
+    tensor carried across steps (zeros before the first); `out_src`, if
+    given, is an int64 [batch] device tensor receiving the 64-bit masks."""
+    import torch
+    i32 = _i32()
+    _check("pld_fuse", load().pld_fuse(
+        ctx, ctypes.byref(params), _dev_ptr(lookup, "lookup", i32), int(lookup_k),
+        _dev_ptr(lookup_len, "lookup_len", i32), _dev_ptr(lookup_match, "lookup_match", i32),
+        _dev_ptr(drafter, "drafter", i32), _dev_ptr(accepted, "accepted", i32),
+        _dev_ptr(state, "state", i32), int(batch), _dev_ptr(out_block, "out_block", i32),
+        _dev_ptr(out_positions, "out_positions", i32),
+        _dev_ptr(out_src, "out_src", torch.int64), _stream(stream)))
 
 
 def pld_sync(ctx: int, stream=None) -> int:

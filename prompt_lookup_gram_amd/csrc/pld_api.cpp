@@ -331,6 +331,80 @@ pld_status pld_draft_batch_strided(pld_ctx *ctx, const int32_t *base, int64_t st
                  out_draft, out_len, out_match, out_pos, stream);
 }
 
+pld_status pld_fuse_params_default(pld_fuse_params *params)
+{
+    if (!params)
+        return fail(PLD_EINVAL, "params is null");
+    // HyperQwen lookup-drafting page, steps 2 and 3: a 7-token drafter head,
+    // 15 draft positions in a long block, replace at a match of 8 (6 with 2
+    // agreeing tokens), fill the tail at 4, enter after 2 near-full steps,
+    // hold 3; near-full = at most 1 position short (a reading)
+    *params = pld_fuse_params{7, 15, 8, 6, 2, 4, 2, 3, 1};
+    return PLD_OK;
+}
+
+pld_status pld_fuse(pld_ctx *ctx, const pld_fuse_params *params, const int32_t *lookup,
+                    int32_t lookup_k, const int32_t *lookup_len, const int32_t *lookup_match,
+                    const int32_t *drafter, const int32_t *accepted, int32_t *state,
+                    int32_t batch, int32_t *out_block, int32_t *out_positions,
+                    uint64_t *out_src, hipStream_t stream)
+{
+    if (!ctx)
+        return fail(PLD_EINVAL, "ctx is null");
+    if (!params)
+        return fail(PLD_EINVAL, "params is null");
+    const pld_fuse_params &p = *params;
+    if (p.head < 1 || p.positions_long < p.head || p.positions_long > PLD_FUSE_MAX_POSITIONS)
+        return fail(PLD_EINVAL, "need 1 <= head <= positions_long <= %d (got %d, %d)",
+                    PLD_FUSE_MAX_POSITIONS, p.head, p.positions_long);
+    if (p.agree_tokens < 1 || p.agree_tokens > p.head)
+        return fail(PLD_EINVAL, "need 1 <= agree_tokens <= head (got %d)", p.agree_tokens);
+    if (p.replace_min < 1 || p.agree_min < 1 || p.tail_min < 1)
+        return fail(PLD_EINVAL, "match thresholds must be >= 1");
+    if (p.entry_steps < 0 || p.sticky < 0 || p.near_full_slack < 0)
+        return fail(PLD_EINVAL, "entry_steps, sticky and near_full_slack must be >= 0");
+    if (lookup_k < 1)
+        return fail(PLD_EINVAL, "lookup_k must be >= 1 (got %d)", lookup_k);
+    if (batch < 0 || batch > ctx->max_batch)
+        return fail(PLD_EINVAL, "batch %d outside [0, max_batch=%d]", batch, ctx->max_batch);
+    if (batch == 0)
+        return PLD_OK;
+    if (!lookup || !lookup_len || !lookup_match || !drafter || !accepted || !state ||
+        !out_block || !out_positions)
+        return fail(PLD_EINVAL, "null buffer pointer");
+    if (((uintptr_t)lookup | (uintptr_t)lookup_len | (uintptr_t)lookup_match |
+         (uintptr_t)drafter | (uintptr_t)accepted | (uintptr_t)state | (uintptr_t)out_block |
+         (uintptr_t)out_positions) & 3u)
+        return fail(PLD_EINVAL, "int32 buffers must be 4-byte aligned");
+    if ((uintptr_t)out_src & 7u)
+        return fail(PLD_EINVAL, "out_src must be 8-byte aligned");
+    pld::FuseArgs a;
+    a.head = p.head;
+    a.positions_long = p.positions_long;
+    a.replace_min = p.replace_min;
+    a.agree_min = p.agree_min;
+    a.agree_tokens = p.agree_tokens;
+    a.tail_min = p.tail_min;
+    a.entry_steps = p.entry_steps;
+    a.sticky = p.sticky;
+    a.near_full_slack = p.near_full_slack;
+    a.lookup = lookup;
+    a.lookup_k = lookup_k;
+    a.lookup_len = lookup_len;
+    a.lookup_match = lookup_match;
+    a.drafter = drafter;
+    a.accepted = accepted;
+    a.state = state;
+    a.out_block = out_block;
+    a.out_positions = out_positions;
+    a.out_src = (unsigned long long *)out_src;
+    a.err = ctx->err;
+    hipError_t e = pld::launch_fuse(a, batch, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "fuse kernel launch");
+    return PLD_OK;
+}
+
 pld_status pld_sync(pld_ctx *ctx, hipStream_t stream)
 {
     if (!ctx)
@@ -350,11 +424,12 @@ pld_status pld_sync(pld_ctx *ctx, hipStream_t stream)
                     (bits & pld::kErrLenCapacity) ? "a history longer than max_len " : "",
                     (bits & pld::kErrAppendCapacity) ? "an append past max_len" : "");
     if (bits)
-        return fail(PLD_EINVAL, "device reported: %s%s%s%s",
+        return fail(PLD_EINVAL, "device reported: %s%s%s%s%s",
                     (bits & pld::kErrLenNegative) ? "a negative length " : "",
                     (bits & pld::kErrBadRow) ? "a null or misaligned row pointer " : "",
                     (bits & pld::kErrAppendNegative) ? "a negative append count " : "",
-                    (bits & pld::kErrBelowMinLen) ? "a length below the promised min_len" : "");
+                    (bits & pld::kErrBelowMinLen) ? "a length below the promised min_len " : "",
+                    (bits & pld::kErrFuseInput) ? "inconsistent fusion inputs" : "");
     return PLD_OK;
 }
 

@@ -19,7 +19,8 @@ enum : uint32_t {
     kErrBadRow = 4u,          // null or misaligned row pointer with L > 0
     kErrAppendCapacity = 8u,  // append would pass max_len
     kErrAppendNegative = 16u, // counts[b] < 0
-    kErrBelowMinLen = 32u     // strided batch: lengths[b] < the caller's min_len
+    kErrBelowMinLen = 32u,    // strided batch: lengths[b] < the caller's min_len
+    kErrFuseInput = 64u       // pld_fuse: inconsistent per-request inputs
 };
 
 // Per-request reduction state: the packed key maximum and the arrival
@@ -61,12 +62,31 @@ struct AppendArgs {
     unsigned int *err;
 };
 
+// Draft fusion and long-block scheduling (pld_fuse): parameters as in
+// pld_fuse_params, then the per-request buffers.
+struct FuseArgs {
+    int32_t head, positions_long, replace_min, agree_min, agree_tokens, tail_min;
+    int32_t entry_steps, sticky, near_full_slack;
+    const int32_t *lookup;        // [batch * lookup_k]
+    int32_t lookup_k;
+    const int32_t *lookup_len;    // [batch]
+    const int32_t *lookup_match;  // [batch]
+    const int32_t *drafter;       // [batch * head]
+    const int32_t *accepted;      // [batch]
+    int32_t *state;               // [batch * 4]
+    int32_t *out_block;           // [batch * positions_long]
+    int32_t *out_positions;       // [batch]
+    unsigned long long *out_src;  // [batch] or null
+    unsigned int *err;
+};
+
 // Workgroups the scan launches for a batch (tiles per request x batch).
 int64_t scan_grid(int32_t max_len, int32_t batch, int tile_tokens);
 
 hipError_t launch_draft(const DraftArgs &a, int tile_tokens, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, int32_t batch, hipStream_t s);
 hipError_t launch_fill(int32_t *p, int64_t n, int32_t value, hipStream_t s);
+hipError_t launch_fuse(const FuseArgs &a, int32_t batch, hipStream_t s);
 
 }  // namespace pld
 

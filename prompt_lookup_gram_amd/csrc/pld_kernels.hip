@@ -600,6 +600,83 @@ __global__ __launch_bounds__(256) void pld_fill_i32(int32_t *p, int64_t n, int32
         p[i] = value;
 }
 
+// Draft fusion and long-block scheduling for one request per wavefront
+// (HyperQwen lookup-drafting page, steps 2 and 3); lane t owns block
+// position t. In the page's order: the run of near-full steps is brought up
+// to date with the previous step's accepted count, the block size is
+// chosen (entry condition, or the sticky hold), then the head is fused and
+// the tail filled from the lookup draft.
+__global__ __launch_bounds__(kWave) void pld_fuse_kernel(FuseArgs a)
+{
+    const int b = blockIdx.x;
+    const int t = threadIdx.x;
+    const int32_t d = a.lookup_len[b];
+    const int32_t m = a.lookup_match[b];
+    int32_t *st = a.state + (int64_t)b * 4;
+    const int32_t was_long = st[0];
+    int32_t hold = st[1];
+    int32_t streak = st[2];
+    const int32_t prev_n = st[3];
+    const int32_t acc = a.accepted[b];
+    const bool ok = d >= 0 && d <= a.lookup_k && m >= 0 && hold >= 0 && streak >= 0 &&
+                    prev_n >= 0 && prev_n <= PLD_FUSE_MAX_POSITIONS &&
+                    (prev_n == 0 || (acc >= 0 && acc <= prev_n));
+    // tokens of this lane's position (lookup only where its draft has one)
+    const int32_t dr = t < a.head ? a.drafter[(int64_t)b * a.head + t] : -1;
+    const int32_t lk = ok && t < d ? a.lookup[(int64_t)b * a.lookup_k + t] : -1;
+
+    int32_t n = a.head;
+    int32_t is_long = 0;
+    bool from_lookup = false;
+    if (ok) {
+        // step 3: near-full run, entry condition, sticky hold
+        if (prev_n > 0) {
+            // only "at least entry_steps" matters, so the run is capped there
+            const bool near_full = acc >= prev_n - a.near_full_slack;
+            const int32_t run = streak < a.entry_steps ? streak + 1 : a.entry_steps;
+            streak = near_full ? run : 0;
+        }
+        const bool fills_tail = m >= a.tail_min && d >= a.positions_long;
+        if (fills_tail && streak >= a.entry_steps) {
+            is_long = 1;
+            hold = a.sticky;
+        } else if (was_long != 0 && hold > 0) {
+            is_long = 1;
+            hold -= 1;
+        } else {
+            hold = 0;
+        }
+        // step 2: the head, replaced outright or on agreement of the first
+        // agree_tokens tokens (each of which the lookup draft must have)
+        const u64 agree_mask = a.agree_tokens >= kWave ? ~0ull : (1ull << a.agree_tokens) - 1;
+        const u64 eq = __ballot(t < a.agree_tokens && t < d && dr == lk);
+        const bool agree = (eq & agree_mask) == agree_mask;
+        const bool replace = m >= a.replace_min || (m >= a.agree_min && agree);
+        if (is_long && m >= a.tail_min) {
+            const int32_t cover = d < a.positions_long ? d : a.positions_long;
+            n = cover > a.head ? cover : a.head;
+        }
+        from_lookup = t < a.head ? (replace && t < d) : t < n;
+    } else {
+        streak = 0;
+        hold = 0;
+    }
+    const u64 src = __ballot(from_lookup);
+    if (t < a.positions_long)
+        a.out_block[(int64_t)b * a.positions_long + t] = t >= n ? -1 : (from_lookup ? lk : dr);
+    if (t == 0) {
+        a.out_positions[b] = n;
+        if (a.out_src)
+            a.out_src[b] = src;
+        st[0] = is_long;
+        st[1] = hold;
+        st[2] = streak;
+        st[3] = ok ? n : 0;
+        if (!ok)
+            atomicOr(a.err, kErrFuseInput);
+    }
+}
+
 template <int TILE, int THREADS>
 hipError_t launch_scan(const DraftArgs &a, int64_t tiles_per_req, hipStream_t s)
 {
@@ -655,6 +732,14 @@ hipError_t launch_fill(int32_t *p, int64_t n, int32_t value, hipStream_t s)
         return hipSuccess;
     const int64_t blocks = (n + 255) / 256;
     hipLaunchKernelGGL(pld_fill_i32, dim3((unsigned)blocks), dim3(256), 0, s, p, n, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_fuse(const FuseArgs &a, int32_t batch, hipStream_t s)
+{
+    if (batch <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(pld_fuse_kernel, dim3((unsigned)batch), dim3(kWave), 0, s, a);
     return hipGetLastError();
 }
 

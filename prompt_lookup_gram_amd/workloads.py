@@ -271,3 +271,37 @@ def fuzz_batch(seed: int, max_batch: int = 24, max_len: int = 5000):
 
 
 ALL_CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4}
+
+
+# ---------------------------------------------------------------------------
+# draft fusion inputs (random draws only; nothing here fuses or schedules)
+# ---------------------------------------------------------------------------
+
+#: field order of the fusion parameters (pld_fuse_params)
+FUSE_PARAM_FIELDS = ("head", "positions_long", "replace_min", "agree_min", "agree_tokens",
+                     "tail_min", "entry_steps", "sticky", "near_full_slack")
+
+
+def fuse_params_draw(rng: np.random.Generator) -> dict:
+    """Random fusion parameters covering small and page-sized blocks."""
+    head = int(rng.integers(1, 9))
+    return dict(head=head, positions_long=int(rng.integers(head, 17)),
+                replace_min=int(rng.integers(1, 13)), agree_min=int(rng.integers(1, 13)),
+                agree_tokens=int(rng.integers(1, head + 1)), tail_min=int(rng.integers(1, 13)),
+                entry_steps=int(rng.integers(0, 4)), sticky=int(rng.integers(0, 5)),
+                near_full_slack=int(rng.integers(0, 3)))
+
+
+def fuse_step_draws(rng: np.random.Generator, batch: int, head: int, lookup_k: int = 16,
+                    alphabet: int = 3):
+    """One step of random lookup results and drafter proposals, over a small
+    alphabet so that agreement, every match length and full tails all occur:
+    (lookup [batch, lookup_k] with -1 past each draft, draft lengths,
+    match lengths, drafter [batch, head]). The drafter may propose -1, a
+    legal token that is also the lookup row's padding value."""
+    m = rng.integers(0, 13, size=batch).astype(np.int32)
+    d = np.where(m > 0, rng.integers(1, lookup_k + 1, size=batch), 0).astype(np.int32)
+    lookup = rng.integers(0, alphabet, size=(batch, lookup_k)).astype(np.int32)
+    lookup[np.arange(lookup_k)[None, :] >= d[:, None]] = -1
+    drafter = rng.integers(-1, alphabet, size=(batch, head)).astype(np.int32)
+    return lookup, d, m, drafter

@@ -79,3 +79,19 @@ def test_python_wrapper_raises_with_detail():
     with pytest.raises(B.PldError) as e:
         B.pld_create(0, 5)
     assert e.value.status == B.PLD_EINVAL and "max_batch" in str(e.value)
+
+
+def test_fuse_params_default_is_the_page_setting():
+    """HyperQwen lookup-drafting page, steps 2 and 3: 7-token drafter head,
+    15 draft positions, 8 / 6 with 2 agreeing / 4, two near-full steps, hold
+    3; near-full slack 1 is the reading taken where the page gives no number."""
+    p = B.pld_fuse_params_default()
+    assert [getattr(p, f) for f, _ in p._fields_] == [7, 15, 8, 6, 2, 4, 2, 3, 1]
+    assert _raw("pld_fuse_params_default", None) == B.PLD_EINVAL
+
+
+def test_fuse_null_context_or_params_rejected():
+    p = B.pld_fuse_params_default()
+    args = (None, 16, None, None, None, None, None, 0, None, None, None, None)
+    assert _raw("pld_fuse", None, ctypes.byref(p), *args) == B.PLD_EINVAL
+    assert "ctx is null" in B.pld_last_error()

@@ -21,6 +21,7 @@ import numpy as np
 import pytest
 
 import oracle
+from prompt_lookup_gram_amd import workloads as wl
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "fuse_cases.txt")
 K_LOOKUP = 16
@@ -98,28 +99,15 @@ def test_golden_cover_every_rule():
 
 
 def random_params(rng):
-    head = int(rng.integers(1, 9))
-    return oracle.FuseParams(
-        head=head, positions_long=int(rng.integers(head, 17)),
-        replace_min=int(rng.integers(1, 13)), agree_min=int(rng.integers(1, 13)),
-        agree_tokens=int(rng.integers(1, head + 1)), tail_min=int(rng.integers(1, 13)),
-        entry_steps=int(rng.integers(0, 4)), sticky=int(rng.integers(0, 5)),
-        near_full_slack=int(rng.integers(0, 3)))
+    return oracle.FuseParams(**wl.fuse_params_draw(rng))
 
 
 def random_trace(rng, params, batch, steps):
-    """Random lookup results and drafter proposals over a small alphabet, so
-    that agreement, matches of every length and full tails all occur. Yields
-    per step (lookup, d, m, drafter); accepted counts are drawn by the caller
-    from the previous block's positions."""
+    """Random lookup results and drafter proposals (the shared seeded
+    generator); accepted counts are drawn by run_trace from the previous
+    block's positions."""
     for _ in range(steps):
-        m = rng.integers(0, 13, size=batch).astype(np.int32)
-        d = np.where(m > 0, rng.integers(1, K_LOOKUP + 1, size=batch), 0).astype(np.int32)
-        lookup = rng.integers(0, 3, size=(batch, K_LOOKUP)).astype(np.int32)
-        lookup[np.arange(K_LOOKUP)[None, :] >= d[:, None]] = -1
-        # -1 is a legal token too (it is also the lookup row's padding)
-        drafter = rng.integers(-1, 3, size=(batch, params.head)).astype(np.int32)
-        yield lookup, d, m, drafter
+        yield wl.fuse_step_draws(rng, batch, params.head, K_LOOKUP)
 
 
 def run_trace(params, trace, rng, batch, lib=None):
