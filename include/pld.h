@@ -267,6 +267,20 @@ pld_status pld_fuse(pld_ctx *ctx, const pld_fuse_params *params, const int32_t *
                     uint64_t *out_src, hipStream_t stream);
 
 /*
+ * pld_draft_batch followed by pld_fuse on its outputs, in one launch: the
+ * workgroup that emits a request's lookup draft also fuses it with the
+ * drafter's proposal (lookup_k = k_max). Outputs of both calls are written;
+ * arguments and errors are those of the two calls.
+ */
+pld_status pld_draft_fuse_batch(pld_ctx *ctx, const int32_t *const *histories,
+                                const int32_t *lengths, int32_t batch, int32_t n_min,
+                                int32_t n_max, int32_t k_max, int32_t *out_draft,
+                                int32_t *out_len, int32_t *out_match,
+                                const pld_fuse_params *params, const int32_t *drafter,
+                                const int32_t *accepted, int32_t *state, int32_t *out_block,
+                                int32_t *out_positions, uint64_t *out_src, hipStream_t stream);
+
+/*
  * Wait for the stream, then report and clear the sticky device-side flag:
  * PLD_OK when clear; PLD_ECAPACITY when a history exceeded max_len (or its
  * row's stride) or an append overflowed; PLD_EINVAL when a length or count

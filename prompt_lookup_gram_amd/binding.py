@@ -30,7 +30,8 @@ PLD_FUSE_MAX_POSITIONS = 64
 EXPORTS = ("pld_create", "pld_destroy", "pld_configure", "pld_append",
            "pld_store_views", "pld_store_reset", "pld_draft_batch",
            "pld_draft_batch_pos", "pld_draft_batch_strided", "pld_fuse_params_default",
-           "pld_fuse", "pld_sync", "pld_strerror", "pld_last_error")
+           "pld_fuse", "pld_draft_fuse_batch", "pld_sync", "pld_strerror",
+           "pld_last_error")
 
 _lib = None
 
@@ -73,6 +74,8 @@ def load(path: str = LIB_PATH):
         "pld_fuse_params_default": [ctypes.POINTER(PldFuseParams)],
         "pld_fuse": [vp, ctypes.POINTER(PldFuseParams), vp, i32, vp, vp, vp, vp, vp, i32,
                      vp, vp, vp, vp],
+        "pld_draft_fuse_batch": [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp,
+                                 ctypes.POINTER(PldFuseParams), vp, vp, vp, vp, vp, vp, vp],
         "pld_sync": [vp, vp],
     }
     for name, args in sig.items():
@@ -239,6 +242,23 @@ def pld_fuse(ctx: int, params: PldFuseParams, lookup, lookup_k: int, lookup_len,
         _dev_ptr(drafter, "drafter", i32), _dev_ptr(accepted, "accepted", i32),
         _dev_ptr(state, "state", i32), int(batch), _dev_ptr(out_block, "out_block", i32),
         _dev_ptr(out_positions, "out_positions", i32),
+        _dev_ptr(out_src, "out_src", torch.int64), _stream(stream)))
+
+
+def pld_draft_fuse_batch(ctx: int, histories, lengths, batch: int, n_min: int, n_max: int,
+                         k_max: int, out_draft, out_len, out_match, params: PldFuseParams,
+                         drafter, accepted, state, out_block, out_positions, out_src=None,
+                         stream=None) -> None:
+    """pld_draft_batch and pld_fuse in one launch (include/pld.h)."""
+    import torch
+    i32 = _i32()
+    _check("pld_draft_fuse_batch", load().pld_draft_fuse_batch(
+        ctx, _dev_ptr(histories, "histories"), _dev_ptr(lengths, "lengths", i32), int(batch),
+        int(n_min), int(n_max), int(k_max), _dev_ptr(out_draft, "out_draft", i32),
+        _dev_ptr(out_len, "out_len", i32), _dev_ptr(out_match, "out_match", i32),
+        ctypes.byref(params), _dev_ptr(drafter, "drafter", i32),
+        _dev_ptr(accepted, "accepted", i32), _dev_ptr(state, "state", i32),
+        _dev_ptr(out_block, "out_block", i32), _dev_ptr(out_positions, "out_positions", i32),
         _dev_ptr(out_src, "out_src", torch.int64), _stream(stream)))
 
 

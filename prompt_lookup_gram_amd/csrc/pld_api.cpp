@@ -98,7 +98,7 @@ pld_status draft(pld_ctx *ctx, const int32_t *const *histories, const int32_t *b
                  int64_t stride, int32_t min_len, const int32_t *lengths,
                  int32_t batch, int32_t n_min, int32_t n_max, int32_t k_max,
                  int32_t *out_draft, int32_t *out_len, int32_t *out_match,
-                 int32_t *out_pos, hipStream_t stream)
+                 int32_t *out_pos, hipStream_t stream, const pld::FuseArgs *fuse = nullptr)
 {
     // a strided batch stands in for the row table in the common checks
     const int32_t *const *rows_or_base =
@@ -138,9 +138,71 @@ pld_status draft(pld_ctx *ctx, const int32_t *const *histories, const int32_t *b
     a.slots = ctx->slots;
     a.err = ctx->err;
     a.zero16 = ctx->zero16;
+    a.do_fuse = fuse != nullptr;
+    if (fuse)
+        a.fuse = *fuse;
+    else
+        memset(&a.fuse, 0, sizeof(a.fuse));
     hipError_t e = pld::launch_draft(a, ctx->tile_tokens, stream);
     if (e != hipSuccess)
         return hip_fail(e, "draft kernel launch");
+    return PLD_OK;
+}
+
+// Checks a fusion step's arguments and fills `a`; PLD_OK or the failure.
+pld_status fuse_args(pld_ctx *ctx, const pld_fuse_params *params, const int32_t *lookup,
+                     int32_t lookup_k, const int32_t *lookup_len, const int32_t *lookup_match,
+                     const int32_t *drafter, const int32_t *accepted, int32_t *state,
+                     int32_t batch, int32_t *out_block, int32_t *out_positions,
+                     uint64_t *out_src, pld::FuseArgs &a)
+{
+    if (!ctx)
+        return fail(PLD_EINVAL, "ctx is null");
+    if (!params)
+        return fail(PLD_EINVAL, "params is null");
+    const pld_fuse_params &p = *params;
+    if (p.head < 1 || p.positions_long < p.head || p.positions_long > PLD_FUSE_MAX_POSITIONS)
+        return fail(PLD_EINVAL, "need 1 <= head <= positions_long <= %d (got %d, %d)",
+                    PLD_FUSE_MAX_POSITIONS, p.head, p.positions_long);
+    if (p.agree_tokens < 1 || p.agree_tokens > p.head)
+        return fail(PLD_EINVAL, "need 1 <= agree_tokens <= head (got %d)", p.agree_tokens);
+    if (p.replace_min < 1 || p.agree_min < 1 || p.tail_min < 1)
+        return fail(PLD_EINVAL, "match thresholds must be >= 1");
+    if (p.entry_steps < 0 || p.sticky < 0 || p.near_full_slack < 0)
+        return fail(PLD_EINVAL, "entry_steps, sticky and near_full_slack must be >= 0");
+    if (lookup_k < 1)
+        return fail(PLD_EINVAL, "lookup_k must be >= 1 (got %d)", lookup_k);
+    if (batch < 0 || batch > ctx->max_batch)
+        return fail(PLD_EINVAL, "batch %d outside [0, max_batch=%d]", batch, ctx->max_batch);
+    if (batch > 0 && (!lookup || !lookup_len || !lookup_match || !drafter || !accepted ||
+                      !state || !out_block || !out_positions))
+        return fail(PLD_EINVAL, "null buffer pointer");
+    if (((uintptr_t)lookup | (uintptr_t)lookup_len | (uintptr_t)lookup_match |
+         (uintptr_t)drafter | (uintptr_t)accepted | (uintptr_t)state | (uintptr_t)out_block |
+         (uintptr_t)out_positions) & 3u)
+        return fail(PLD_EINVAL, "int32 buffers must be 4-byte aligned");
+    if ((uintptr_t)out_src & 7u)
+        return fail(PLD_EINVAL, "out_src must be 8-byte aligned");
+    a.head = p.head;
+    a.positions_long = p.positions_long;
+    a.replace_min = p.replace_min;
+    a.agree_min = p.agree_min;
+    a.agree_tokens = p.agree_tokens;
+    a.tail_min = p.tail_min;
+    a.entry_steps = p.entry_steps;
+    a.sticky = p.sticky;
+    a.near_full_slack = p.near_full_slack;
+    a.lookup = lookup;
+    a.lookup_k = lookup_k;
+    a.lookup_len = lookup_len;
+    a.lookup_match = lookup_match;
+    a.drafter = drafter;
+    a.accepted = accepted;
+    a.state = state;
+    a.out_block = out_block;
+    a.out_positions = out_positions;
+    a.out_src = (unsigned long long *)out_src;
+    a.err = ctx->err;
     return PLD_OK;
 }
 
@@ -349,60 +411,35 @@ pld_status pld_fuse(pld_ctx *ctx, const pld_fuse_params *params, const int32_t *
                     int32_t batch, int32_t *out_block, int32_t *out_positions,
                     uint64_t *out_src, hipStream_t stream)
 {
-    if (!ctx)
-        return fail(PLD_EINVAL, "ctx is null");
-    if (!params)
-        return fail(PLD_EINVAL, "params is null");
-    const pld_fuse_params &p = *params;
-    if (p.head < 1 || p.positions_long < p.head || p.positions_long > PLD_FUSE_MAX_POSITIONS)
-        return fail(PLD_EINVAL, "need 1 <= head <= positions_long <= %d (got %d, %d)",
-                    PLD_FUSE_MAX_POSITIONS, p.head, p.positions_long);
-    if (p.agree_tokens < 1 || p.agree_tokens > p.head)
-        return fail(PLD_EINVAL, "need 1 <= agree_tokens <= head (got %d)", p.agree_tokens);
-    if (p.replace_min < 1 || p.agree_min < 1 || p.tail_min < 1)
-        return fail(PLD_EINVAL, "match thresholds must be >= 1");
-    if (p.entry_steps < 0 || p.sticky < 0 || p.near_full_slack < 0)
-        return fail(PLD_EINVAL, "entry_steps, sticky and near_full_slack must be >= 0");
-    if (lookup_k < 1)
-        return fail(PLD_EINVAL, "lookup_k must be >= 1 (got %d)", lookup_k);
-    if (batch < 0 || batch > ctx->max_batch)
-        return fail(PLD_EINVAL, "batch %d outside [0, max_batch=%d]", batch, ctx->max_batch);
-    if (batch == 0)
-        return PLD_OK;
-    if (!lookup || !lookup_len || !lookup_match || !drafter || !accepted || !state ||
-        !out_block || !out_positions)
-        return fail(PLD_EINVAL, "null buffer pointer");
-    if (((uintptr_t)lookup | (uintptr_t)lookup_len | (uintptr_t)lookup_match |
-         (uintptr_t)drafter | (uintptr_t)accepted | (uintptr_t)state | (uintptr_t)out_block |
-         (uintptr_t)out_positions) & 3u)
-        return fail(PLD_EINVAL, "int32 buffers must be 4-byte aligned");
-    if ((uintptr_t)out_src & 7u)
-        return fail(PLD_EINVAL, "out_src must be 8-byte aligned");
     pld::FuseArgs a;
-    a.head = p.head;
-    a.positions_long = p.positions_long;
-    a.replace_min = p.replace_min;
-    a.agree_min = p.agree_min;
-    a.agree_tokens = p.agree_tokens;
-    a.tail_min = p.tail_min;
-    a.entry_steps = p.entry_steps;
-    a.sticky = p.sticky;
-    a.near_full_slack = p.near_full_slack;
-    a.lookup = lookup;
-    a.lookup_k = lookup_k;
-    a.lookup_len = lookup_len;
-    a.lookup_match = lookup_match;
-    a.drafter = drafter;
-    a.accepted = accepted;
-    a.state = state;
-    a.out_block = out_block;
-    a.out_positions = out_positions;
-    a.out_src = (unsigned long long *)out_src;
-    a.err = ctx->err;
+    pld_status st = fuse_args(ctx, params, lookup, lookup_k, lookup_len, lookup_match, drafter,
+                              accepted, state, batch, out_block, out_positions, out_src, a);
+    if (st != PLD_OK || batch == 0)
+        return st;
     hipError_t e = pld::launch_fuse(a, batch, stream);
     if (e != hipSuccess)
         return hip_fail(e, "fuse kernel launch");
     return PLD_OK;
+}
+
+pld_status pld_draft_fuse_batch(pld_ctx *ctx, const int32_t *const *histories,
+                                const int32_t *lengths, int32_t batch, int32_t n_min,
+                                int32_t n_max, int32_t k_max, int32_t *out_draft,
+                                int32_t *out_len, int32_t *out_match,
+                                const pld_fuse_params *params, const int32_t *drafter,
+                                const int32_t *accepted, int32_t *state, int32_t *out_block,
+                                int32_t *out_positions, uint64_t *out_src, hipStream_t stream)
+{
+    if (ctx && k_max < 1)
+        return fail(PLD_EINVAL, "k_max must be >= 1 (got %d)", k_max);
+    // the lookup draft the fusion reads is this call's own output row
+    pld::FuseArgs f;
+    pld_status st = fuse_args(ctx, params, out_draft, k_max, out_len, out_match, drafter,
+                              accepted, state, batch, out_block, out_positions, out_src, f);
+    if (st != PLD_OK)
+        return st;
+    return draft(ctx, histories, nullptr, 0, 0, lengths, batch, n_min, n_max, k_max, out_draft,
+                 out_len, out_match, nullptr, stream, &f);
 }
 
 pld_status pld_sync(pld_ctx *ctx, hipStream_t stream)

@@ -32,6 +32,24 @@ struct alignas(256) ReqSlot {
     unsigned int pad[61];
 };
 
+// Draft fusion and long-block scheduling (pld_fuse): parameters as in
+// pld_fuse_params, then the per-request buffers.
+struct FuseArgs {
+    int32_t head, positions_long, replace_min, agree_min, agree_tokens, tail_min;
+    int32_t entry_steps, sticky, near_full_slack;
+    const int32_t *lookup;        // [batch * lookup_k]
+    int32_t lookup_k;
+    const int32_t *lookup_len;    // [batch]
+    const int32_t *lookup_match;  // [batch]
+    const int32_t *drafter;       // [batch * head]
+    const int32_t *accepted;      // [batch]
+    int32_t *state;               // [batch * 4]
+    int32_t *out_block;           // [batch * positions_long]
+    int32_t *out_positions;       // [batch]
+    unsigned long long *out_src;  // [batch] or null
+    unsigned int *err;
+};
+
 struct DraftArgs {
     const int32_t *const *histories;  // row table (stride == 0)
     const int32_t *base;              // strided batch: row b at base + b * stride
@@ -49,6 +67,8 @@ struct DraftArgs {
     ReqSlot *slots;                // [max_batch], zero between calls
     unsigned int *err;             // sticky error word
     const int4 *zero16;            // 16 zero bytes (edge-chunk load target)
+    FuseArgs fuse;                 // the fusion step, when do_fuse
+    int32_t do_fuse;               // emit also fuses (pld_draft_fuse_batch)
 };
 
 struct AppendArgs {
@@ -59,24 +79,6 @@ struct AppendArgs {
     int64_t pitch;
     int32_t *lengths;
     int32_t max_len;
-    unsigned int *err;
-};
-
-// Draft fusion and long-block scheduling (pld_fuse): parameters as in
-// pld_fuse_params, then the per-request buffers.
-struct FuseArgs {
-    int32_t head, positions_long, replace_min, agree_min, agree_tokens, tail_min;
-    int32_t entry_steps, sticky, near_full_slack;
-    const int32_t *lookup;        // [batch * lookup_k]
-    int32_t lookup_k;
-    const int32_t *lookup_len;    // [batch]
-    const int32_t *lookup_match;  // [batch]
-    const int32_t *drafter;       // [batch * head]
-    const int32_t *accepted;      // [batch]
-    int32_t *state;               // [batch * 4]
-    int32_t *out_block;           // [batch * positions_long]
-    int32_t *out_positions;       // [batch]
-    unsigned long long *out_src;  // [batch] or null
     unsigned int *err;
 };
 

@@ -172,6 +172,122 @@ __device__ __forceinline__ void emit(const DraftArgs &a, int b, const Req &r,
     }
 }
 
+// Draft fusion and long-block scheduling of request b by one wavefront
+// (HyperQwen lookup-drafting page, steps 2 and 3); lane t owns block
+// position t and holds the lookup draft's token t in `lk` (t < d). In the
+// page's order: the run of near-full steps is brought up to date with the
+// previous step's accepted count, the block size is chosen (entry
+// condition, or the sticky hold), then the head is fused and the tail
+// filled from the lookup draft.
+__device__ __forceinline__ void fuse_request(const FuseArgs &a, int b, int t, int32_t d,
+                                             int32_t m, int32_t lk)
+{
+    int32_t *st = a.state + (int64_t)b * 4;
+    const int32_t was_long = st[0];
+    int32_t hold = st[1];
+    int32_t streak = st[2];
+    const int32_t prev_n = st[3];
+    const int32_t acc = a.accepted[b];
+    const bool ok = d >= 0 && d <= a.lookup_k && m >= 0 && hold >= 0 && streak >= 0 &&
+                    prev_n >= 0 && prev_n <= PLD_FUSE_MAX_POSITIONS &&
+                    (prev_n == 0 || (acc >= 0 && acc <= prev_n));
+    const int32_t dr = t < a.head ? a.drafter[(int64_t)b * a.head + t] : -1;
+
+    int32_t n = a.head;
+    int32_t is_long = 0;
+    bool from_lookup = false;
+    if (ok) {
+        // step 3: near-full run, entry condition, sticky hold
+        if (prev_n > 0) {
+            // only "at least entry_steps" matters, so the run is capped there
+            const bool near_full = acc >= prev_n - a.near_full_slack;
+            const int32_t run = streak < a.entry_steps ? streak + 1 : a.entry_steps;
+            streak = near_full ? run : 0;
+        }
+        const bool fills_tail = m >= a.tail_min && d >= a.positions_long;
+        if (fills_tail && streak >= a.entry_steps) {
+            is_long = 1;
+            hold = a.sticky;
+        } else if (was_long != 0 && hold > 0) {
+            is_long = 1;
+            hold -= 1;
+        } else {
+            hold = 0;
+        }
+        // step 2: the head, replaced outright or on agreement of the first
+        // agree_tokens tokens (each of which the lookup draft must have)
+        const u64 agree_mask = a.agree_tokens >= kWave ? ~0ull : (1ull << a.agree_tokens) - 1;
+        const u64 eq = __ballot(t < a.agree_tokens && t < d && dr == lk);
+        const bool agree = (eq & agree_mask) == agree_mask;
+        const bool replace = m >= a.replace_min || (m >= a.agree_min && agree);
+        if (is_long && m >= a.tail_min) {
+            const int32_t cover = d < a.positions_long ? d : a.positions_long;
+            n = cover > a.head ? cover : a.head;
+        }
+        from_lookup = t < a.head ? (replace && t < d) : t < n;
+    } else {
+        streak = 0;
+        hold = 0;
+    }
+    const u64 src = __ballot(from_lookup);
+    if (t < a.positions_long)
+        a.out_block[(int64_t)b * a.positions_long + t] = t >= n ? -1 : (from_lookup ? lk : dr);
+    if (t == 0) {
+        a.out_positions[b] = n;
+        if (a.out_src)
+            a.out_src[b] = src;
+        st[0] = is_long;
+        st[1] = hold;
+        st[2] = streak;
+        st[3] = ok ? n : 0;
+        if (!ok)
+            atomicOr(a.err, kErrFuseInput);
+    }
+}
+
+// Writes row b of the lookup outputs (as emit does) and fuses them with the
+// drafter's proposal (fuse_request) in one wavefront: lane t holds the
+// lookup draft's token t. Used instead of emit when the call also fuses.
+__device__ __forceinline__ void emit_and_fuse(const DraftArgs &a, int b, const Req &r, u64 key,
+                                              int lane)
+{
+    int32_t m = 0, d = 0, e = -1;
+    if (key != 0) {
+        m = (int32_t)(key >> 32);
+        e = (int32_t)(key & 0xffffffffu);
+        const int32_t follow = r.L - 1 - e;
+        d = follow < a.k_max ? follow : a.k_max;
+    }
+    int32_t *row = a.out_draft + (int64_t)b * a.k_max;
+    const int32_t *src = r.h + (int64_t)e + 1;
+    const int32_t lk = lane < d ? gld(src + lane) : -1;
+    if (lane < a.k_max)
+        row[lane] = lk;
+    for (int t = lane + kWave; t < a.k_max; t += kWave)
+        row[t] = t < d ? gld(src + t) : -1;
+    if (lane == 0) {
+        a.out_len[b] = d;
+        a.out_match[b] = m;
+        if (a.out_pos)
+            a.out_pos[b] = key != 0 ? e - m + 1 : -1;
+    }
+    fuse_request(a.fuse, b, lane, d, m, lk);
+}
+
+// The emit step of a request by the workgroup that holds its final key:
+// lookup outputs only, or lookup outputs and fusion (wavefront 0).
+__device__ __forceinline__ void emit_request(const DraftArgs &a, int b, const Req &r, u64 key,
+                                             int tid, int nthreads)
+{
+    if (a.do_fuse) {
+        if (tid < kWave)
+            emit_and_fuse(a, b, r, key, tid);
+    } else {
+        emit(a, b, r, key, tid, nthreads);
+    }
+}
+
+
 // A 16-byte chunk covering positions p0 .. p0+3 is loaded whole when all
 // four positions lie in [0, L). Chunks at the row's edges (p0 < 0 or past
 // the end) are first loaded from a 16-byte zero block owned by the context,
@@ -545,7 +661,7 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
     }
     __syncthreads();
     if (s_last)
-        emit(a, b, r, wg_best, tid, THREADS);
+        emit_request(a, b, r, wg_best, tid, THREADS);
 }
 
 __global__ __launch_bounds__(kWave) void pld_gather(DraftArgs a)
@@ -553,7 +669,7 @@ __global__ __launch_bounds__(kWave) void pld_gather(DraftArgs a)
     const int b = blockIdx.x;
     const Req r = load_req(a, b, 1);
     const u64 key = a.slots[b].key;
-    emit(a, b, r, r.err ? 0ull : key, threadIdx.x, kWave);
+    emit_request(a, b, r, r.err ? 0ull : key, threadIdx.x, kWave);
     __syncthreads();
     if (threadIdx.x == 0 && key != 0)
         a.slots[b].key = 0;
@@ -600,81 +716,17 @@ __global__ __launch_bounds__(256) void pld_fill_i32(int32_t *p, int64_t n, int32
         p[i] = value;
 }
 
-// Draft fusion and long-block scheduling for one request per wavefront
-// (HyperQwen lookup-drafting page, steps 2 and 3); lane t owns block
-// position t. In the page's order: the run of near-full steps is brought up
-// to date with the previous step's accepted count, the block size is
-// chosen (entry condition, or the sticky hold), then the head is fused and
-// the tail filled from the lookup draft.
+// pld_fuse: one wavefront per request, lookup drafts read from the caller's
+// buffers.
 __global__ __launch_bounds__(kWave) void pld_fuse_kernel(FuseArgs a)
 {
     const int b = blockIdx.x;
     const int t = threadIdx.x;
     const int32_t d = a.lookup_len[b];
     const int32_t m = a.lookup_match[b];
-    int32_t *st = a.state + (int64_t)b * 4;
-    const int32_t was_long = st[0];
-    int32_t hold = st[1];
-    int32_t streak = st[2];
-    const int32_t prev_n = st[3];
-    const int32_t acc = a.accepted[b];
-    const bool ok = d >= 0 && d <= a.lookup_k && m >= 0 && hold >= 0 && streak >= 0 &&
-                    prev_n >= 0 && prev_n <= PLD_FUSE_MAX_POSITIONS &&
-                    (prev_n == 0 || (acc >= 0 && acc <= prev_n));
-    // tokens of this lane's position (lookup only where its draft has one)
-    const int32_t dr = t < a.head ? a.drafter[(int64_t)b * a.head + t] : -1;
-    const int32_t lk = ok && t < d ? a.lookup[(int64_t)b * a.lookup_k + t] : -1;
-
-    int32_t n = a.head;
-    int32_t is_long = 0;
-    bool from_lookup = false;
-    if (ok) {
-        // step 3: near-full run, entry condition, sticky hold
-        if (prev_n > 0) {
-            // only "at least entry_steps" matters, so the run is capped there
-            const bool near_full = acc >= prev_n - a.near_full_slack;
-            const int32_t run = streak < a.entry_steps ? streak + 1 : a.entry_steps;
-            streak = near_full ? run : 0;
-        }
-        const bool fills_tail = m >= a.tail_min && d >= a.positions_long;
-        if (fills_tail && streak >= a.entry_steps) {
-            is_long = 1;
-            hold = a.sticky;
-        } else if (was_long != 0 && hold > 0) {
-            is_long = 1;
-            hold -= 1;
-        } else {
-            hold = 0;
-        }
-        // step 2: the head, replaced outright or on agreement of the first
-        // agree_tokens tokens (each of which the lookup draft must have)
-        const u64 agree_mask = a.agree_tokens >= kWave ? ~0ull : (1ull << a.agree_tokens) - 1;
-        const u64 eq = __ballot(t < a.agree_tokens && t < d && dr == lk);
-        const bool agree = (eq & agree_mask) == agree_mask;
-        const bool replace = m >= a.replace_min || (m >= a.agree_min && agree);
-        if (is_long && m >= a.tail_min) {
-            const int32_t cover = d < a.positions_long ? d : a.positions_long;
-            n = cover > a.head ? cover : a.head;
-        }
-        from_lookup = t < a.head ? (replace && t < d) : t < n;
-    } else {
-        streak = 0;
-        hold = 0;
-    }
-    const u64 src = __ballot(from_lookup);
-    if (t < a.positions_long)
-        a.out_block[(int64_t)b * a.positions_long + t] = t >= n ? -1 : (from_lookup ? lk : dr);
-    if (t == 0) {
-        a.out_positions[b] = n;
-        if (a.out_src)
-            a.out_src[b] = src;
-        st[0] = is_long;
-        st[1] = hold;
-        st[2] = streak;
-        st[3] = ok ? n : 0;
-        if (!ok)
-            atomicOr(a.err, kErrFuseInput);
-    }
+    const int32_t lk = d >= 0 && d <= a.lookup_k && t < d ? a.lookup[(int64_t)b * a.lookup_k + t]
+                                                          : -1;
+    fuse_request(a, b, t, d, m, lk);
 }
 
 template <int TILE, int THREADS>

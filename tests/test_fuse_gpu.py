@@ -231,3 +231,87 @@ def test_fuse_host_validation():
         assert B.pld_sync(ctx) == B.PLD_OK
     finally:
         B.pld_destroy(ctx)
+
+
+# ---------------------------------------------------------------------------
+# pld_draft_fuse_batch: lookup drafting and fusion in one launch
+# ---------------------------------------------------------------------------
+
+PAGE = dict(zip(wl.FUSE_PARAM_FIELDS, [7, 15, 8, 6, 2, 4, 2, 3, 1]))
+
+
+def run_one_launch(w, steps, seed, tile=0, fused=-1, params=PAGE, k=None):
+    """`steps` decode steps of pld_draft_fuse_batch on one batch (the same
+    histories each step, new drafter proposals and accepted counts), against
+    oracle.draft followed by oracle.fuse."""
+    import torch
+    k = k or w.k_max
+    rng = np.random.default_rng([7104, seed])
+    db = B.DeviceBatch(w.histories)
+    ctx = B.pld_create(max(1, w.batch), db.max_len)
+    op = oracle.FuseParams(**params)
+    n = params["positions_long"]
+    od, ol, om, _ = oracle.draft(w.histories, w.n_min, w.n_max, k)
+    state = torch.zeros((w.batch, W), dtype=torch.int32, device="cuda")
+    ostate = np.zeros((w.batch, W), np.int32)
+    prev_pos = np.zeros(w.batch, np.int32)
+    try:
+        B.pld_configure(ctx, tile, fused)
+        for step in range(steps):
+            drafter = rng.integers(0, 40, size=(w.batch, params["head"])).astype(np.int32)
+            agree = rng.random(w.batch) < 0.5
+            a = min(params["agree_tokens"], k)
+            drafter[agree, :a] = od[agree, :a]
+            acc = np.array([rng.integers(max(0, p - 2), p + 1) for p in prev_pos], np.int32)
+            out = B.alloc_outputs(w.batch, k)
+            for t in out:
+                t.fill_(-7)
+            blk = torch.full((w.batch, n), -7, dtype=torch.int32, device="cuda")
+            pos = torch.full((w.batch,), -7, dtype=torch.int32, device="cuda")
+            src = torch.full((w.batch,), -7, dtype=torch.int64, device="cuda")
+            B.pld_draft_fuse_batch(ctx, db.rows, db.lengths, w.batch, w.n_min, w.n_max, k,
+                                   out[0], out[1], out[2], gpu_params(params), to_dev(drafter),
+                                   to_dev(acc), state, blk, pos, src)
+            assert B.pld_sync(ctx) == B.PLD_OK
+            ob, opos, osrc, ostate = oracle.fuse(op, od, ol, om, drafter, acc, ostate)
+            label = f"{w.name} tile={tile} fused={fused} step={step}"
+            assert np.array_equal(out[0].cpu().numpy(), od), label
+            assert np.array_equal(out[1].cpu().numpy(), ol), label
+            assert np.array_equal(out[2].cpu().numpy(), om), label
+            gb = blk.cpu().numpy()
+            bad = np.nonzero(np.any(gb != ob, axis=1))[0]
+            assert bad.size == 0, f"{label}: block of b={bad[:1]} {gb[bad[:1]]} vs {ob[bad[:1]]}"
+            assert np.array_equal(pos.cpu().numpy(), opos), label
+            assert np.array_equal(src.cpu().numpy().view(np.uint64), osrc), label
+            assert np.array_equal(state.cpu().numpy(), ostate), label
+            prev_pos = opos
+        return ostate
+    finally:
+        B.pld_destroy(ctx)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+@pytest.mark.parametrize("tile,fused", [(0, -1), (256, 1), (256, 0), (16384, 1), (1024, 0)])
+def test_draft_fuse_one_launch(cfg, tile, fused):
+    """Every emit site fuses: single-tile requests, the last workgroup of a
+    split request, and the separate gather kernel."""
+    w = wl.ALL_CONFIGS[cfg]()
+    st = run_one_launch(w, steps=5, seed=cfg, tile=tile, fused=fused)
+    if cfg in (1, 2):
+        assert (st[:, 0] == 1).any(), "copy tails reach long blocks"
+
+
+def test_draft_fuse_one_launch_long_rows():
+    """64 workgroups per request at the 262,144-token rows."""
+    run_one_launch(wl.config4(), steps=3, seed=4)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_draft_fuse_one_launch_fuzz(seed):
+    """Random batches (tiny and empty histories included), random
+    parameters, k_max below and above the long block."""
+    w = wl.fuzz_batch(100 + seed)
+    params = wl.fuse_params_draw(np.random.default_rng([7105, seed]))
+    for k in (max(1, params["positions_long"] - 3), params["positions_long"] + 5, 70):
+        run_one_launch(w, steps=4, seed=seed, params=params, k=k,
+                       tile=(256, 1024)[seed % 2], fused=seed % 2)
