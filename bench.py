@@ -38,6 +38,8 @@ if ROOT not in sys.path:
 
 METRIC = ("batched draft steps/s + scanned history GB/s (% HBM peak); "
           "p50 µs per draft step")
+METRIC_FUSE = ("lookup draft + draft fusion and long-block scheduling steps/s "
+               "(HyperQwen lookup-drafting page, steps 1-3)")
 PROFILE = os.path.join(ROOT, "profiles", "pld_scan_c4_b16x262144.md")
 KERNEL_SRC = os.path.join(ROOT, "prompt_lookup_gram_amd", "csrc", "pld_kernels.hip")
 
@@ -83,6 +85,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true",
                     help="also time without buffer rotation (cache-resident)")
+    ap.add_argument("--fuse", choices=["none", "one", "two"], default="none",
+                    help="each step also fuses the lookup draft with a drafter's "
+                         "proposal and schedules the block (one launch: "
+                         "pld_draft_fuse_batch; two: pld_draft_batch + pld_fuse); "
+                         "row-table layout, workloads 1-4")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with 8 plain 64 MiB device copies (a counter "
                          "reference of known size for rocprofv3 --pmc)")
@@ -123,6 +130,8 @@ def main():
         return bench_stream(args, torch, B, wl, dev)
 
     w = wl.ALL_CONFIGS[args.config]()
+    if args.fuse != "none":
+        return bench_fuse(args, torch, B, wl, dev, w)
     bytes_step = 4 * w.total_tokens
     # enough copies to defeat the Infinity Cache, capped for the tiny batches
     # (which are launch-latency bound either way)
@@ -298,6 +307,156 @@ def main():
                       f"{len(os.sched_getaffinity(0))} host cores visible)",
             "effective_GBps": round(bytes_step * n / el / 1e9, 3),
         }
+        rec["parity"] = "bit-exact" if parity else "MISMATCH"
+        if not parity:
+            print(json.dumps(rec))
+            sys.exit(1)
+    print(json.dumps(rec), flush=True)
+
+
+def bench_fuse(args, torch, B, wl, dev, w):
+    """Lookup drafting plus draft fusion and long-block scheduling per step.
+
+    Each step drafts the batch (rotated copies, as the plain bench) and fuses
+    the drafts with a drafter's 7-token proposal under the page's parameters,
+    the schedule state carried on the device. Drafter proposals are seeded
+    draws; each step's accepted count is drawn against the previous block's
+    positions in one untimed eager pass (mostly near-full, as while copying),
+    so the graph of G steps (state zeroed first) replays exactly that pass.
+    """
+    import torch as _t
+    bytes_step = 4 * w.total_tokens
+    rot = min(64, max(1, -(-2 * MALL_BYTES // bytes_step)))
+    G = max(1, min(args.graph_steps, args.steps))
+    k = w.k_max
+    params = B.pld_fuse_params_default()
+    n_pos = params.positions_long
+    base = B.DeviceBatch(w.histories, device=dev)
+    copies = [base] + [base.replicate() for _ in range(rot - 1)]
+    rows_all = _t.stack([c.rows for c in copies]).contiguous()
+    ctx = B.pld_create(w.batch, base.max_len)
+    B.pld_configure(ctx, args.tile, args.fused)
+    out = B.alloc_outputs(w.batch, k, device=dev)
+    state = _t.zeros((w.batch, B.PLD_FUSE_STATE_WORDS), dtype=_t.int32, device=dev)
+    blk = _t.empty((w.batch, n_pos), dtype=_t.int32, device=dev)
+    pos = _t.empty(w.batch, dtype=_t.int32, device=dev)
+    src = _t.empty(w.batch, dtype=_t.int64, device=dev)
+    rng = np.random.default_rng([8001, args.config])
+    drafter = rng.integers(0, wl.ZIPF_VOCAB, size=(G, w.batch, params.head)).astype(np.int32)
+    drafter_d = _t.from_numpy(drafter).to(dev)
+    acc = np.zeros((G, w.batch), np.int32)
+    acc_d = _t.zeros((G, w.batch), dtype=_t.int32, device=dev)
+
+    def call(i, stream=None):
+        r = i % rot
+        if args.fuse == "one":
+            B.pld_draft_fuse_batch(ctx, rows_all[r], copies[r].lengths, w.batch, w.n_min,
+                                   w.n_max, k, out[0], out[1], out[2], params, drafter_d[i % G],
+                                   acc_d[i % G], state, blk, pos, src, stream=stream)
+        else:
+            B.pld_draft_batch(ctx, rows_all[r], copies[r].lengths, w.batch, w.n_min, w.n_max,
+                              k, out[0], out[1], out[2], stream=stream)
+            B.pld_fuse(ctx, params, out[0], k, out[1], out[2], drafter_d[i % G], acc_d[i % G],
+                       state, w.batch, blk, pos, src, stream=stream)
+
+    # untimed eager pass: fixes each step's accepted count
+    trace = []
+    for i in range(G):
+        acc_d[i].copy_(_t.from_numpy(acc[i]))
+        call(i)
+        p_ = pos.cpu().numpy()
+        trace.append((out[0].cpu().numpy(), out[1].cpu().numpy(), out[2].cpu().numpy(),
+                      blk.cpu().numpy(), p_, src.cpu().numpy(), state.cpu().numpy()))
+        if i + 1 < G:
+            short = rng.choice([0, 0, 0, 1, 1, 2, 4, 7], size=w.batch)
+            acc[i + 1] = np.maximum(p_ - short, 0)
+    assert B.pld_sync(ctx) == B.PLD_OK
+    long_frac = float(np.mean([t[6][:, 0] for t in trace]))
+    mean_pos = float(np.mean([t[4] for t in trace]))
+
+    cap_stream = _t.cuda.Stream()
+    graph = _t.cuda.CUDAGraph()
+    _t.cuda.synchronize()
+    with _t.cuda.graph(graph, stream=cap_stream):
+        state.zero_()
+        for i in range(G):
+            call(i)
+    _t.cuda.synchronize()
+    for _ in range(3):  # every replay reproduces the eager pass's last step
+        blk.fill_(-9)
+        graph.replay()
+        _t.cuda.synchronize()
+        assert np.array_equal(blk.cpu().numpy(), trace[-1][3]), "graph replay differs"
+        assert np.array_equal(state.cpu().numpy(), trace[-1][6]), "graph replay differs"
+    reps_w = max(1, args.warmup // G)
+    reps = max(1, -(-args.steps // G))
+    steps = reps * G
+    for _ in range(reps_w):
+        graph.replay()
+    _t.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0, ev1 = _t.cuda.Event(enable_timing=True), _t.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        graph.replay()
+    ev1.record()
+    _t.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    gpu_us = ev0.elapsed_time(ev1) * 1e3 / steps
+    assert B.pld_sync(ctx) == B.PLD_OK
+    B.pld_destroy(ctx)
+    scan_gbps = bytes_step / (gpu_us * 1e-6) / 1e9
+    launches = 1 if args.fuse == "one" else 2
+    rec = {
+        "metric": METRIC_FUSE,
+        "value": round(steps / wall_s, 1),
+        "unit": "draft+fuse steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": reps_w * G,
+        "ms_per_step": round(wall_s * 1e3 / steps, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "layout": "rows",
+                   "history_tokens": int(w.lengths.max()), "n_min": w.n_min,
+                   "n_max": w.n_max, "k_max": k, "bytes_per_step": bytes_step,
+                   "rotated_copies": rot, "graph_steps": G,
+                   "fuse": {f: getattr(params, f) for f, _ in params._fields_},
+                   "launches_per_step": launches},
+        "graph_us_per_step": round(gpu_us, 3),
+        "scan_GBps": round(scan_gbps, 1),
+        "hbm_frac": round(scan_gbps / HBM_PEAK_GBPS, 4),
+        "long_block_step_frac": round(long_frac, 4),
+        "mean_draft_positions": round(mean_pos, 3),
+        "roofline": {"bound": "hbm", "achieved": round(scan_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(scan_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "kernel": "pld_scan" + (" + pld_fuse_kernel"
+                                                              if launches == 2 else ""),
+                     "time_source": f"HIP events around the timed graph replays ({steps} "
+                                    f"steps, {launches} launch(es) each, state zeroed "
+                                    f"once per {G} steps)"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        op = oracle.FuseParams(*[getattr(params, f) for f, _ in params._fields_])
+        ostate = np.zeros((w.batch, B.PLD_FUSE_STATE_WORDS), np.int32)
+        n, parity, t_start = 0, True, time.perf_counter()
+        while n < G and time.perf_counter() - t_start < args.cpu_seconds:
+            od, ol, om, _ = oracle.draft(w.histories, w.n_min, w.n_max, k)
+            ob, opos, osrc, ostate = oracle.fuse(op, od, ol, om, drafter[n], acc[n], ostate)
+            g = trace[n]
+            parity &= all(np.array_equal(a_, b_) for a_, b_ in
+                          zip((od, ol, om, ob, opos, osrc.view(np.int64), ostate), g))
+            n += 1
+        el = time.perf_counter() - t_start
+        rec["cpu_baseline"] = {
+            "value": round(n / el, 3), "unit": "draft+fuse steps/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the first {n} steps (lookup oracle then fusion oracle, {el:.1f} s, "
+                      f"one thread, {cpu_model()})"}
         rec["parity"] = "bit-exact" if parity else "MISMATCH"
         if not parity:
             print(json.dumps(rec))

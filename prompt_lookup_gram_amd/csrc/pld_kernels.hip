@@ -179,19 +179,43 @@ __device__ __forceinline__ void emit(const DraftArgs &a, int b, const Req &r,
 // previous step's accepted count, the block size is chosen (entry
 // condition, or the sticky hold), then the head is fused and the tail
 // filled from the lookup draft.
+// The inputs of a request's fusion step that do not depend on its lookup
+// draft: its state row, its accepted count and lane t's drafter token. The
+// scan kernel reads them before it scans, so they are at hand when the
+// draft is.
+struct FusePre {
+    int32_t was_long, hold, streak, prev_n, acc, dr;
+};
+
+__device__ __forceinline__ FusePre fuse_preload(const FuseArgs &a, int b, int t)
+{
+    const int32_t *st = a.state + (int64_t)b * 4;
+    FusePre p;
+    p.was_long = st[0];
+    p.hold = st[1];
+    p.streak = st[2];
+    p.prev_n = st[3];
+    p.acc = a.accepted[b];
+    // every lane loads (lanes past the head re-read the last head token), so
+    // no load sits inside a branch
+    const int32_t dr = a.drafter[(int64_t)b * a.head + (t < a.head ? t : a.head - 1)];
+    p.dr = t < a.head ? dr : -1;
+    return p;
+}
+
 __device__ __forceinline__ void fuse_request(const FuseArgs &a, int b, int t, int32_t d,
-                                             int32_t m, int32_t lk)
+                                             int32_t m, int32_t lk, const FusePre &pre)
 {
     int32_t *st = a.state + (int64_t)b * 4;
-    const int32_t was_long = st[0];
-    int32_t hold = st[1];
-    int32_t streak = st[2];
-    const int32_t prev_n = st[3];
-    const int32_t acc = a.accepted[b];
+    const int32_t was_long = pre.was_long;
+    int32_t hold = pre.hold;
+    int32_t streak = pre.streak;
+    const int32_t prev_n = pre.prev_n;
+    const int32_t acc = pre.acc;
     const bool ok = d >= 0 && d <= a.lookup_k && m >= 0 && hold >= 0 && streak >= 0 &&
                     prev_n >= 0 && prev_n <= PLD_FUSE_MAX_POSITIONS &&
                     (prev_n == 0 || (acc >= 0 && acc <= prev_n));
-    const int32_t dr = t < a.head ? a.drafter[(int64_t)b * a.head + t] : -1;
+    const int32_t dr = pre.dr;
 
     int32_t n = a.head;
     int32_t is_long = 0;
@@ -249,7 +273,7 @@ __device__ __forceinline__ void fuse_request(const FuseArgs &a, int b, int t, in
 // drafter's proposal (fuse_request) in one wavefront: lane t holds the
 // lookup draft's token t. Used instead of emit when the call also fuses.
 __device__ __forceinline__ void emit_and_fuse(const DraftArgs &a, int b, const Req &r, u64 key,
-                                              int lane)
+                                              int lane, const FusePre &pre)
 {
     int32_t m = 0, d = 0, e = -1;
     if (key != 0) {
@@ -271,17 +295,18 @@ __device__ __forceinline__ void emit_and_fuse(const DraftArgs &a, int b, const R
         if (a.out_pos)
             a.out_pos[b] = key != 0 ? e - m + 1 : -1;
     }
-    fuse_request(a.fuse, b, lane, d, m, lk);
+    fuse_request(a.fuse, b, lane, d, m, lk, pre);
 }
 
 // The emit step of a request by the workgroup that holds its final key:
 // lookup outputs only, or lookup outputs and fusion (wavefront 0).
+template <bool FUSE>
 __device__ __forceinline__ void emit_request(const DraftArgs &a, int b, const Req &r, u64 key,
-                                             int tid, int nthreads)
+                                             int tid, int nthreads, const FusePre &pre)
 {
-    if (a.do_fuse) {
+    if constexpr (FUSE) {
         if (tid < kWave)
-            emit_and_fuse(a, b, r, key, tid);
+            emit_and_fuse(a, b, r, key, tid, pre);
     } else {
         emit(a, b, r, key, tid, nthreads);
     }
@@ -543,7 +568,7 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
 // caller's bound min_len (checked against each length on the device) then
 // issues its loads at once, before its length is read from memory; other
 // tiles, and row-table batches, read the length and row first.
-template <int TILE, int THREADS, bool STRIDED>
+template <int TILE, int THREADS, bool STRIDED, bool FUSE>
 __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int32_t *lengths,
                                                     int32_t batch, int32_t max_len,
                                                     int32_t n_min, int32_t n_max, int64_t stride,
@@ -591,6 +616,9 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
     }
 
     const Req r = load_req(a, b, TILE);
+    FusePre pre{};
+    if constexpr (FUSE)
+        pre = fuse_preload(a.fuse, b, tid & (kWave - 1));
     if (tile >= r.ntiles)
         return;  // this request has no candidates in this tile
     if (r.err && tid == 0)
@@ -661,7 +689,7 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
     }
     __syncthreads();
     if (s_last)
-        emit_request(a, b, r, wg_best, tid, THREADS);
+        emit_request<FUSE>(a, b, r, wg_best, tid, THREADS, pre);
 }
 
 __global__ __launch_bounds__(kWave) void pld_gather(DraftArgs a)
@@ -669,7 +697,11 @@ __global__ __launch_bounds__(kWave) void pld_gather(DraftArgs a)
     const int b = blockIdx.x;
     const Req r = load_req(a, b, 1);
     const u64 key = a.slots[b].key;
-    emit_request(a, b, r, r.err ? 0ull : key, threadIdx.x, kWave);
+    if (a.do_fuse)
+        emit_request<true>(a, b, r, r.err ? 0ull : key, threadIdx.x, kWave,
+                           fuse_preload(a.fuse, b, threadIdx.x));
+    else
+        emit_request<false>(a, b, r, r.err ? 0ull : key, threadIdx.x, kWave, FusePre{});
     __syncthreads();
     if (threadIdx.x == 0 && key != 0)
         a.slots[b].key = 0;
@@ -726,21 +758,27 @@ __global__ __launch_bounds__(kWave) void pld_fuse_kernel(FuseArgs a)
     const int32_t m = a.lookup_match[b];
     const int32_t lk = d >= 0 && d <= a.lookup_k && t < d ? a.lookup[(int64_t)b * a.lookup_k + t]
                                                           : -1;
-    fuse_request(a, b, t, d, m, lk);
+    fuse_request(a, b, t, d, m, lk, fuse_preload(a, b, t));
 }
 
 template <int TILE, int THREADS>
 hipError_t launch_scan(const DraftArgs &a, int64_t tiles_per_req, hipStream_t s)
 {
     const int64_t grid = tiles_per_req * a.batch;
+    if (a.stride && a.do_fuse)
+        return hipErrorInvalidValue;  // no entry point fuses a strided batch
     if (a.stride)
-        hipLaunchKernelGGL((pld_scan<TILE, THREADS, true>), dim3((unsigned)grid), dim3(THREADS), 0,
-                           s, (const void *)a.base, a.lengths, a.batch, a.max_len, a.n_min,
-                           a.n_max, a.stride, a.min_len, a);
+        hipLaunchKernelGGL((pld_scan<TILE, THREADS, true, false>), dim3((unsigned)grid),
+                           dim3(THREADS), 0, s, (const void *)a.base, a.lengths, a.batch,
+                           a.max_len, a.n_min, a.n_max, a.stride, a.min_len, a);
+    else if (a.do_fuse && a.fused)
+        hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, true>), dim3((unsigned)grid),
+                           dim3(THREADS), 0, s, (const void *)a.histories, a.lengths, a.batch,
+                           a.max_len, a.n_min, a.n_max, (int64_t)0, 0, a);
     else
-        hipLaunchKernelGGL((pld_scan<TILE, THREADS, false>), dim3((unsigned)grid), dim3(THREADS), 0,
-                           s, (const void *)a.histories, a.lengths, a.batch, a.max_len, a.n_min,
-                           a.n_max, (int64_t)0, 0, a);
+        hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, false>), dim3((unsigned)grid),
+                           dim3(THREADS), 0, s, (const void *)a.histories, a.lengths, a.batch,
+                           a.max_len, a.n_min, a.n_max, (int64_t)0, 0, a);
     return hipGetLastError();
 }
 
