@@ -83,6 +83,24 @@ typedef enum pld_status {
 pld_status pld_create(pld_ctx **out, int32_t max_batch, int32_t max_len,
                       int32_t own_store);
 
+/*
+ * pld_create with a store (own_store = 1) and an incremental n-gram index
+ * over it, for lengths n_min..n_max (1 <= n_min <= n_max <= PLD_N_MAX_LIMIT).
+ *
+ * The Strata prompt-lookup page (section 4) keeps an index from n-grams to
+ * history positions that grows by O(1) work per appended token. Here, for
+ * each request and each indexed length n, an open-addressed table maps every
+ * n-gram of the history to the end of its most recent occurrence that can be
+ * drafted from. pld_append keeps it current; pld_draft_store answers from it
+ * with exactly the results pld_draft_batch gives on the same store.
+ * Memory: max_batch * (n_max - n_min + 1) tables of 8-byte slots, each table
+ * a power of two >= 2 * max_len slots (576 MB for 64 requests of 49,152
+ * tokens and lengths 4..12).
+ * Errors: as pld_create; PLD_EINVAL for a bad length range.
+ */
+pld_status pld_create_indexed(pld_ctx **out, int32_t max_batch, int32_t max_len,
+                              int32_t n_min, int32_t n_max);
+
 /* Free everything the context owns. Waits for the device to finish work
    first. NULL is a no-op. */
 pld_status pld_destroy(pld_ctx *ctx);
@@ -108,7 +126,9 @@ pld_status pld_configure(pld_ctx *ctx, int32_t tile_tokens, int32_t fused_gather
  *  counts: device int32[batch], each 0 <= counts[b].
  * A row whose append would pass max_len, or whose count is negative, is left
  * unchanged and sets the sticky flag (PLD_ECAPACITY / PLD_EINVAL at
- * pld_sync). batch == 0 is a no-op.
+ * pld_sync). batch == 0 is a no-op. With an index (pld_create_indexed) the
+ * n-grams that the append makes draftable are inserted first, in a second
+ * kernel on the same stream.
  * Errors: PLD_EINVAL (no store, batch outside [0, max_batch], null pointers,
  * negative stride), PLD_EHIP.
  */
@@ -124,8 +144,8 @@ pld_status pld_append(pld_ctx *ctx, const int32_t *tokens, int64_t tokens_stride
 pld_status pld_store_views(pld_ctx *ctx, const int32_t *const **histories,
                            const int32_t **lengths);
 
-/* Set every store row's length to 0 (stream-ordered). Errors: PLD_EINVAL
-   (no store), PLD_EHIP. */
+/* Set every store row's length to 0, and empty the n-gram index if there is
+   one (stream-ordered). Errors: PLD_EINVAL (no store), PLD_EHIP. */
 pld_status pld_store_reset(pld_ctx *ctx, hipStream_t stream);
 
 /*
@@ -184,6 +204,20 @@ pld_status pld_draft_batch_strided(pld_ctx *ctx, const int32_t *base, int64_t st
                                    int32_t n_min, int32_t n_max, int32_t k_max,
                                    int32_t *out_draft, int32_t *out_len, int32_t *out_match,
                                    int32_t *out_pos, hipStream_t stream);
+
+/*
+ * pld_draft_batch over the first `batch` rows of the context's store,
+ * answered from the n-gram index instead of a scan of the histories: one
+ * probe per length n in [n_min, n_max], in parallel, each confirmed against
+ * the stored tokens. Results are identical to pld_draft_batch_pos on
+ * pld_store_views (same outputs, same padding).
+ *  n_min, n_max: within the indexed lengths of pld_create_indexed.
+ *  out_pos: device int32[batch] or NULL.
+ * Errors: PLD_EINVAL (no index, lengths outside it, bad sizes), PLD_EHIP.
+ */
+pld_status pld_draft_store(pld_ctx *ctx, int32_t batch, int32_t n_min, int32_t n_max,
+                           int32_t k_max, int32_t *out_draft, int32_t *out_len,
+                           int32_t *out_match, int32_t *out_pos, hipStream_t stream);
 
 /*
  * Draft fusion and long-block scheduling (HyperQwen lookup-drafting page,

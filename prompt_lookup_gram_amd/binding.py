@@ -27,9 +27,10 @@ PLD_FUSE_STATE_WORDS = 4
 PLD_FUSE_MAX_POSITIONS = 64
 
 # every symbol include/pld.h declares
-EXPORTS = ("pld_create", "pld_destroy", "pld_configure", "pld_append",
+EXPORTS = ("pld_create", "pld_create_indexed", "pld_destroy", "pld_configure", "pld_append",
            "pld_store_views", "pld_store_reset", "pld_draft_batch",
-           "pld_draft_batch_pos", "pld_draft_batch_strided", "pld_fuse_params_default",
+           "pld_draft_batch_pos", "pld_draft_batch_strided", "pld_draft_store",
+           "pld_fuse_params_default",
            "pld_fuse", "pld_draft_fuse_batch", "pld_sync", "pld_strerror",
            "pld_last_error")
 
@@ -62,6 +63,7 @@ def load(path: str = LIB_PATH):
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     sig = {
         "pld_create": [ctypes.POINTER(vp), i32, i32, i32],
+        "pld_create_indexed": [ctypes.POINTER(vp), i32, i32, i32, i32],
         "pld_destroy": [vp],
         "pld_configure": [vp, i32, i32],
         "pld_append": [vp, vp, i64, vp, i32, vp],
@@ -71,6 +73,7 @@ def load(path: str = LIB_PATH):
         "pld_draft_batch_pos": [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp],
         "pld_draft_batch_strided": [vp, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp,
                                     vp, vp],
+        "pld_draft_store": [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp],
         "pld_fuse_params_default": [ctypes.POINTER(PldFuseParams)],
         "pld_fuse": [vp, ctypes.POINTER(PldFuseParams), vp, i32, vp, vp, vp, vp, vp, i32,
                      vp, vp, vp, vp],
@@ -152,6 +155,14 @@ def pld_create(max_batch: int, max_len: int, own_store: bool = False) -> int:
     return ctx.value
 
 
+def pld_create_indexed(max_batch: int, max_len: int, n_min: int, n_max: int) -> int:
+    """A context with a history store and an n-gram index over it."""
+    ctx = ctypes.c_void_p()
+    _check("pld_create_indexed", load().pld_create_indexed(
+        ctypes.byref(ctx), int(max_batch), int(max_len), int(n_min), int(n_max)))
+    return ctx.value
+
+
 def pld_destroy(ctx: int) -> None:
     _check("pld_destroy", load().pld_destroy(ctx))
 
@@ -217,6 +228,17 @@ def pld_draft_batch_strided(ctx: int, base, stride: int, lengths, min_len: int,
     _check("pld_draft_batch_strided", load().pld_draft_batch_strided(
         ctx, _dev_ptr(base, "base", i32), int(stride), _dev_ptr(lengths, "lengths", i32),
         int(min_len), int(batch), int(n_min), int(n_max), int(k_max),
+        _dev_ptr(out_draft, "out_draft", i32), _dev_ptr(out_len, "out_len", i32),
+        _dev_ptr(out_match, "out_match", i32), _dev_ptr(out_pos, "out_pos", i32),
+        _stream(stream)))
+
+
+def pld_draft_store(ctx: int, batch: int, n_min: int, n_max: int, k_max: int, out_draft,
+                    out_len, out_match, out_pos=None, stream=None) -> None:
+    """Draft the store's first `batch` rows from the n-gram index."""
+    i32 = _i32()
+    _check("pld_draft_store", load().pld_draft_store(
+        ctx, int(batch), int(n_min), int(n_max), int(k_max),
         _dev_ptr(out_draft, "out_draft", i32), _dev_ptr(out_len, "out_len", i32),
         _dev_ptr(out_match, "out_match", i32), _dev_ptr(out_pos, "out_pos", i32),
         _stream(stream)))

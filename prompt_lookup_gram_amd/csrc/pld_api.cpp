@@ -27,6 +27,10 @@ struct pld_ctx {
     int64_t pitch;              // tokens per store row
     int32_t *store_len;         // [max_batch] or null
     const int32_t **store_rows; // [max_batch] device row pointers or null
+    unsigned long long *index;  // n-gram index over the store, or null
+    int64_t index_cap;          // slots per (request, length) table
+    int32_t index_lo, index_hi; // indexed lengths
+    int32_t index_chunks;       // workgroups per request for an append's inserts
 };
 
 namespace {
@@ -59,6 +63,7 @@ void release(pld_ctx *c)
     if (c->store) (void)hipFree(c->store);
     if (c->store_len) (void)hipFree(c->store_len);
     if (c->store_rows) (void)hipFree(c->store_rows);
+    if (c->index) (void)hipFree(c->index);
     delete c;
 }
 
@@ -149,6 +154,21 @@ pld_status draft(pld_ctx *ctx, const int32_t *const *histories, const int32_t *b
     return PLD_OK;
 }
 
+pld::IndexArgs index_args(pld_ctx *ctx)
+{
+    pld::IndexArgs a;
+    a.table = ctx->index;
+    a.cap = ctx->index_cap;
+    a.n_lo = ctx->index_lo;
+    a.n_hi = ctx->index_hi;
+    a.store = ctx->store;
+    a.pitch = ctx->pitch;
+    a.lengths = ctx->store_len;
+    a.max_len = ctx->max_len;
+    a.err = ctx->err;
+    return a;
+}
+
 // Checks a fusion step's arguments and fills `a`; PLD_OK or the failure.
 pld_status fuse_args(pld_ctx *ctx, const pld_fuse_params *params, const int32_t *lookup,
                      int32_t lookup_k, const int32_t *lookup_len, const int32_t *lookup_match,
@@ -206,11 +226,9 @@ pld_status fuse_args(pld_ctx *ctx, const pld_fuse_params *params, const int32_t 
     return PLD_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-pld_status pld_create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t own_store)
+// Creates a context; index_lo > 0 adds an n-gram index over the store.
+pld_status create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t own_store,
+                  int32_t index_lo, int32_t index_hi)
 {
     if (!out)
         return fail(PLD_EINVAL, "out is null");
@@ -252,7 +270,30 @@ pld_status pld_create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t
                         max_batch, max_len);
         }
     }
+    if (index_lo > 0) {
+        int64_t cap = 1;
+        while (cap < 2 * (int64_t)max_len)
+            cap <<= 1;
+        const int64_t lens = (int64_t)index_hi - index_lo + 1;
+        const double bytes = (double)nb * (double)lens * (double)cap * 8.0;
+        if (bytes > 9.0e18 ||
+            hipMalloc((void **)&c->index, (size_t)nb * (size_t)lens * (size_t)cap * 8) !=
+                hipSuccess) {
+            (void)hipGetLastError();
+            release(c);
+            return fail(PLD_ENOMEM, "device allocation of the n-gram index (%.0f MB) failed",
+                        bytes / 1e6);
+        }
+        c->index_cap = cap;
+        c->index_lo = index_lo;
+        c->index_hi = index_hi;
+        // an append's inserts spread over up to 16 workgroups per request
+        const int64_t chunks = max_len / 8192;
+        c->index_chunks = (int32_t)(chunks < 1 ? 1 : (chunks > 16 ? 16 : chunks));
+    }
     e = hipMemset(c->slots, 0, nb * sizeof(pld::ReqSlot));
+    if (e == hipSuccess && c->index)
+        e = pld::launch_index_clear(index_args(c), max_batch, nullptr);
     if (e == hipSuccess) e = hipMemset(c->err, 0, sizeof(unsigned int));
     if (e == hipSuccess) e = hipMemset(c->zero16, 0, sizeof(int4));
     if (e == hipSuccess && own_store) {
@@ -276,6 +317,24 @@ pld_status pld_create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t
     }
     *out = c;
     return PLD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pld_status pld_create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t own_store)
+{
+    return create(out, max_batch, max_len, own_store, 0, 0);
+}
+
+pld_status pld_create_indexed(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t n_min,
+                              int32_t n_max)
+{
+    if (n_min < 1 || n_max < n_min || n_max > PLD_N_MAX_LIMIT)
+        return fail(PLD_EINVAL, "need 1 <= n_min <= n_max <= %d (got n_min=%d n_max=%d)",
+                    PLD_N_MAX_LIMIT, n_min, n_max);
+    return create(out, max_batch, max_len, 1, n_min, n_max);
 }
 
 pld_status pld_destroy(pld_ctx *ctx)
@@ -329,7 +388,12 @@ pld_status pld_append(pld_ctx *ctx, const int32_t *tokens, int64_t tokens_stride
     a.lengths = ctx->store_len;
     a.max_len = ctx->max_len;
     a.err = ctx->err;
-    hipError_t e = pld::launch_append(a, batch, stream);
+    hipError_t e = hipSuccess;
+    if (ctx->index)  // before the copy: it reads the old length and the store
+        e = pld::launch_index_insert(index_args(ctx), tokens, tokens_stride, counts, batch,
+                                     ctx->index_chunks, stream);
+    if (e == hipSuccess)
+        e = pld::launch_append(a, batch, stream);
     if (e != hipSuccess)
         return hip_fail(e, "append kernel launch");
     return PLD_OK;
@@ -354,8 +418,39 @@ pld_status pld_store_reset(pld_ctx *ctx, hipStream_t stream)
     if (!ctx->store)
         return fail(PLD_EINVAL, "context was created without a store");
     hipError_t e = pld::launch_fill(ctx->store_len, ctx->max_batch, 0, stream);
+    if (e == hipSuccess && ctx->index)
+        e = pld::launch_index_clear(index_args(ctx), ctx->max_batch, stream);
     if (e != hipSuccess)
         return hip_fail(e, "store reset launch");
+    return PLD_OK;
+}
+
+pld_status pld_draft_store(pld_ctx *ctx, int32_t batch, int32_t n_min, int32_t n_max,
+                           int32_t k_max, int32_t *out_draft, int32_t *out_len,
+                           int32_t *out_match, int32_t *out_pos, hipStream_t stream)
+{
+    if (!ctx)
+        return fail(PLD_EINVAL, "ctx is null");
+    if (!ctx->index)
+        return fail(PLD_EINVAL, "context has no n-gram index (see pld_create_indexed)");
+    if (n_min < ctx->index_lo || n_max < n_min || n_max > ctx->index_hi)
+        return fail(PLD_EINVAL, "need %d <= n_min <= n_max <= %d, the indexed lengths "
+                    "(got n_min=%d n_max=%d)", ctx->index_lo, ctx->index_hi, n_min, n_max);
+    if (k_max < 1)
+        return fail(PLD_EINVAL, "k_max must be >= 1 (got %d)", k_max);
+    if (batch < 0 || batch > ctx->max_batch)
+        return fail(PLD_EINVAL, "batch %d outside [0, max_batch=%d]", batch, ctx->max_batch);
+    if (batch == 0)
+        return PLD_OK;
+    if (!out_draft || !out_len || !out_match)
+        return fail(PLD_EINVAL, "null buffer pointer");
+    if (((uintptr_t)out_draft | (uintptr_t)out_len | (uintptr_t)out_match |
+         (uintptr_t)out_pos) & 3u)
+        return fail(PLD_EINVAL, "outputs must be 4-byte aligned");
+    hipError_t e = pld::launch_index_draft(index_args(ctx), batch, n_min, n_max, k_max,
+                                           out_draft, out_len, out_match, out_pos, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "index draft launch");
     return PLD_OK;
 }
 

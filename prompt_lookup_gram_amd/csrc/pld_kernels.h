@@ -82,6 +82,20 @@ struct AppendArgs {
     unsigned int *err;
 };
 
+// The context store's n-gram index (pld_index.hip): per request and per
+// indexed length n in [n_lo, n_hi], `cap` 64-bit slots of
+// (fingerprint << 32 | end + 1), 0 = empty.
+struct IndexArgs {
+    unsigned long long *table;  // [max_batch][n_hi - n_lo + 1][cap]
+    int64_t cap;                // a power of two >= 2 * max_len
+    int32_t n_lo, n_hi;
+    int32_t *store;             // [max_batch * pitch]
+    int64_t pitch;
+    int32_t *lengths;           // [max_batch]
+    int32_t max_len;
+    unsigned int *err;
+};
+
 // Workgroups the scan launches for a batch (tiles per request x batch).
 int64_t scan_grid(int32_t max_len, int32_t batch, int tile_tokens);
 
@@ -89,6 +103,13 @@ hipError_t launch_draft(const DraftArgs &a, int tile_tokens, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, int32_t batch, hipStream_t s);
 hipError_t launch_fill(int32_t *p, int64_t n, int32_t value, hipStream_t s);
 hipError_t launch_fuse(const FuseArgs &a, int32_t batch, hipStream_t s);
+hipError_t launch_index_insert(const IndexArgs &a, const int32_t *tokens, int64_t tokens_stride,
+                               const int32_t *counts, int32_t batch, int32_t chunks,
+                               hipStream_t s);
+hipError_t launch_index_draft(const IndexArgs &a, int32_t batch, int32_t n_min, int32_t n_max,
+                              int32_t k_max, int32_t *out_draft, int32_t *out_len,
+                              int32_t *out_match, int32_t *out_pos, hipStream_t s);
+hipError_t launch_index_clear(const IndexArgs &a, int32_t batch, hipStream_t s);
 
 }  // namespace pld
 

@@ -95,3 +95,12 @@ def test_fuse_null_context_or_params_rejected():
     args = (None, 16, None, None, None, None, None, 0, None, None, None, None)
     assert _raw("pld_fuse", None, ctypes.byref(p), *args) == B.PLD_EINVAL
     assert "ctx is null" in B.pld_last_error()
+
+
+def test_create_indexed_rejects_bad_lengths_before_any_hip_call():
+    ctx = ctypes.c_void_p()
+    for lo, hi in [(0, 4), (5, 4), (1, 65)]:
+        assert _raw("pld_create_indexed", ctypes.byref(ctx), 4, 100, lo, hi) == B.PLD_EINVAL
+        assert "n_min" in B.pld_last_error()
+    assert _raw("pld_draft_store", None, 1, 4, 12, 16, None, None, None, None,
+                None) == B.PLD_EINVAL
