@@ -90,6 +90,9 @@ def parse():
                          "proposal and schedules the block (one launch: "
                          "pld_draft_fuse_batch; two: pld_draft_batch + pld_fuse); "
                          "row-table layout, workloads 1-4")
+    ap.add_argument("--index", action="store_true",
+                    help="workload 5 only: draft from the context's incremental n-gram "
+                         "index (pld_create_indexed, pld_draft_store) instead of scanning")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with 8 plain 64 MiB device copies (a counter "
                          "reference of known size for rocprofv3 --pmc)")
@@ -473,8 +476,19 @@ def bench_stream(args, torch, B, wl, dev):
     HIP graph and replayed from the same start state."""
     start = wl.config5_start()
     nb, steps_n, width = start.batch, wl.STREAM_STEPS, wl.STREAM_MAX_APPEND
-    ctx = B.pld_create(nb, wl.STREAM_MAX_LEN, own_store=True)
+    if args.index:
+        ctx = B.pld_create_indexed(nb, wl.STREAM_MAX_LEN, start.n_min, start.n_max)
+    else:
+        ctx = B.pld_create(nb, wl.STREAM_MAX_LEN, own_store=True)
     rows, lens = B.pld_store_views(ctx)
+
+    def draft():
+        if args.index:
+            B.pld_draft_store(ctx, nb, start.n_min, start.n_max, start.k_max, out[0], out[1],
+                              out[2])
+        else:
+            B.pld_draft_batch(ctx, rows, lens, nb, start.n_min, start.n_max, start.k_max,
+                              out[0], out[1], out[2])
     init = torch.from_numpy(np.stack(start.histories)).to(dev)
     init_counts = torch.full((nb,), wl.STREAM_START_LEN, dtype=torch.int32, device=dev)
     out = B.alloc_outputs(nb, start.k_max, device=dev)
@@ -491,8 +505,7 @@ def bench_stream(args, torch, B, wl, dev):
     lengths = np.full(nb, wl.STREAM_START_LEN, np.int64)
     total_tokens = 0
     for step in range(steps_n):
-        B.pld_draft_batch(ctx, rows, lens, nb, start.n_min, start.n_max, start.k_max,
-                          out[0], out[1], out[2])
+        draft()
         d, l = out[0].cpu().numpy(), out[1].cpu().numpy()
         first_drafts.append((d.copy(), l.copy(), out[2].cpu().numpy()))
         total_tokens += int(lengths.sum())
@@ -515,8 +528,7 @@ def bench_stream(args, torch, B, wl, dev):
     torch.cuda.synchronize()
     with torch.cuda.graph(graph, stream=cap):
         for step in range(steps_n):
-            B.pld_draft_batch(ctx, rows, lens, nb, start.n_min, start.n_max,
-                              start.k_max, out[0], out[1], out[2])
+            draft()
             B.pld_append(ctx, toks_d[step], width, cnts_d[step], nb)
     times = []
     reps = max(1, args.steps // steps_n) if args.steps >= steps_n else 1
@@ -555,10 +567,14 @@ def bench_stream(args, torch, B, wl, dev):
         "data": "synthetic",
         "config": {"workload": start.name, "batch": nb, "start_tokens": wl.STREAM_START_LEN,
                    "steps": steps_n, "n_min": start.n_min, "n_max": start.n_max,
-                   "k_max": start.k_max, "mean_bytes_per_step": round(bytes_mean)},
+                   "k_max": start.k_max, "mean_bytes_per_step": round(bytes_mean),
+                   "drafting": "n-gram index" if args.index else "scan"},
         "us_per_step_append_plus_draft": round(gpu_s * 1e6 / steps_n, 3),
-        "scan_GBps": round(bytes_mean * steps_n / gpu_s / 1e9, 1),
-        "hbm_frac": round(bytes_mean * steps_n / gpu_s / 1e9 / HBM_PEAK_GBPS, 4),
+        # for the index: the history bytes a scan would have read, per second
+        ("scan_equivalent_GBps" if args.index else "scan_GBps"):
+            round(bytes_mean * steps_n / gpu_s / 1e9, 1),
+        "hbm_frac": None if args.index else
+            round(bytes_mean * steps_n / gpu_s / 1e9 / HBM_PEAK_GBPS, 4),
     }
     if not args.no_cpu_baseline:
         import oracle

@@ -206,11 +206,24 @@ pld_status pld_draft_batch_strided(pld_ctx *ctx, const int32_t *base, int64_t st
                                    int32_t *out_pos, hipStream_t stream);
 
 /*
+ * Fingerprint bits the index keeps (default 32). Two n-grams whose hashes
+ * agree in these bits share a slot; a query that lands on such a shared slot
+ * is answered by an exact scan of that request's history, so results never
+ * change, only speed. Fewer bits make that path common, for testing it.
+ * Takes effect for inserts and queries issued afterwards; change it only on
+ * an empty index (after pld_store_reset) so that all entries agree.
+ * Errors: PLD_EINVAL (no index, bits outside [0, 32]).
+ */
+pld_status pld_index_fingerprint_bits(pld_ctx *ctx, int32_t bits);
+
+/*
  * pld_draft_batch over the first `batch` rows of the context's store,
  * answered from the n-gram index instead of a scan of the histories: one
- * probe per length n in [n_min, n_max], in parallel, each confirmed against
- * the stored tokens. Results are identical to pld_draft_batch_pos on
- * pld_store_views (same outputs, same padding).
+ * probe per length n in [n_min, n_max], in parallel; the longest hit is
+ * confirmed against the stored tokens (a shared-fingerprint slot that does
+ * not confirm sends that request to an exact scan of its row). Results are
+ * identical to pld_draft_batch_pos on pld_store_views (same outputs, same
+ * padding).
  *  n_min, n_max: within the indexed lengths of pld_create_indexed.
  *  out_pos: device int32[batch] or NULL.
  * Errors: PLD_EINVAL (no index, lengths outside it, bad sizes), PLD_EHIP.

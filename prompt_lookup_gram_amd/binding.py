@@ -29,7 +29,8 @@ PLD_FUSE_MAX_POSITIONS = 64
 # every symbol include/pld.h declares
 EXPORTS = ("pld_create", "pld_create_indexed", "pld_destroy", "pld_configure", "pld_append",
            "pld_store_views", "pld_store_reset", "pld_draft_batch",
-           "pld_draft_batch_pos", "pld_draft_batch_strided", "pld_draft_store",
+           "pld_draft_batch_pos", "pld_draft_batch_strided", "pld_index_fingerprint_bits",
+           "pld_draft_store",
            "pld_fuse_params_default",
            "pld_fuse", "pld_draft_fuse_batch", "pld_sync", "pld_strerror",
            "pld_last_error")
@@ -73,6 +74,7 @@ def load(path: str = LIB_PATH):
         "pld_draft_batch_pos": [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp],
         "pld_draft_batch_strided": [vp, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp,
                                     vp, vp],
+        "pld_index_fingerprint_bits": [vp, i32],
         "pld_draft_store": [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp],
         "pld_fuse_params_default": [ctypes.POINTER(PldFuseParams)],
         "pld_fuse": [vp, ctypes.POINTER(PldFuseParams), vp, i32, vp, vp, vp, vp, vp, i32,
@@ -231,6 +233,10 @@ def pld_draft_batch_strided(ctx: int, base, stride: int, lengths, min_len: int,
         _dev_ptr(out_draft, "out_draft", i32), _dev_ptr(out_len, "out_len", i32),
         _dev_ptr(out_match, "out_match", i32), _dev_ptr(out_pos, "out_pos", i32),
         _stream(stream)))
+
+
+def pld_index_fingerprint_bits(ctx: int, bits: int) -> None:
+    _check("pld_index_fingerprint_bits", load().pld_index_fingerprint_bits(ctx, int(bits)))
 
 
 def pld_draft_store(ctx: int, batch: int, n_min: int, n_max: int, k_max: int, out_draft,

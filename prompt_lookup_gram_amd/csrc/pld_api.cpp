@@ -31,6 +31,7 @@ struct pld_ctx {
     int64_t index_cap;          // slots per (request, length) table
     int32_t index_lo, index_hi; // indexed lengths
     int32_t index_chunks;       // workgroups per request for an append's inserts
+    uint32_t index_fp_mask;     // fingerprint bits kept
 };
 
 namespace {
@@ -154,6 +155,10 @@ pld_status draft(pld_ctx *ctx, const int32_t *const *histories, const int32_t *b
     return PLD_OK;
 }
 
+// An indexed append whose rows are at most this many tokens apart takes the
+// one-kernel path (the stride bounds the counts of non-overlapping rows).
+constexpr int64_t kSmallAppend = 1024;
+
 pld::IndexArgs index_args(pld_ctx *ctx)
 {
     pld::IndexArgs a;
@@ -165,6 +170,7 @@ pld::IndexArgs index_args(pld_ctx *ctx)
     a.pitch = ctx->pitch;
     a.lengths = ctx->store_len;
     a.max_len = ctx->max_len;
+    a.fp_mask = ctx->index_fp_mask;
     a.err = ctx->err;
     return a;
 }
@@ -285,6 +291,7 @@ pld_status create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t own
                         bytes / 1e6);
         }
         c->index_cap = cap;
+        c->index_fp_mask = 0xffffffffu;
         c->index_lo = index_lo;
         c->index_hi = index_hi;
         // an append's inserts spread over up to 16 workgroups per request
@@ -389,11 +396,18 @@ pld_status pld_append(pld_ctx *ctx, const int32_t *tokens, int64_t tokens_stride
     a.max_len = ctx->max_len;
     a.err = ctx->err;
     hipError_t e = hipSuccess;
-    if (ctx->index)  // before the copy: it reads the old length and the store
-        e = pld::launch_index_insert(index_args(ctx), tokens, tokens_stride, counts, batch,
-                                     ctx->index_chunks, stream);
-    if (e == hipSuccess)
-        e = pld::launch_append(a, batch, stream);
+    if (ctx->index && tokens_stride > 0 && tokens_stride <= kSmallAppend) {
+        // rows of at most kSmallAppend tokens (a decode loop's appends):
+        // inserts and copy in one workgroup per request
+        e = pld::launch_append_indexed(index_args(ctx), tokens, tokens_stride, counts, batch,
+                                       stream);
+    } else {
+        if (ctx->index)  // before the copy: it reads the old length and the store
+            e = pld::launch_index_insert(index_args(ctx), tokens, tokens_stride, counts, batch,
+                                         ctx->index_chunks, stream);
+        if (e == hipSuccess)
+            e = pld::launch_append(a, batch, stream);
+    }
     if (e != hipSuccess)
         return hip_fail(e, "append kernel launch");
     return PLD_OK;
@@ -422,6 +436,18 @@ pld_status pld_store_reset(pld_ctx *ctx, hipStream_t stream)
         e = pld::launch_index_clear(index_args(ctx), ctx->max_batch, stream);
     if (e != hipSuccess)
         return hip_fail(e, "store reset launch");
+    return PLD_OK;
+}
+
+pld_status pld_index_fingerprint_bits(pld_ctx *ctx, int32_t bits)
+{
+    if (!ctx)
+        return fail(PLD_EINVAL, "ctx is null");
+    if (!ctx->index)
+        return fail(PLD_EINVAL, "context has no n-gram index (see pld_create_indexed)");
+    if (bits < 0 || bits > 32)
+        return fail(PLD_EINVAL, "bits must be in [0, 32] (got %d)", bits);
+    ctx->index_fp_mask = bits == 32 ? 0xffffffffu : ((1u << bits) - 1u);
     return PLD_OK;
 }
 

@@ -19,18 +19,25 @@
 //    most recent start j = e - n + 1.
 //
 // Table entries are 64-bit words (fingerprint << 32 | end + 1); 0 is empty.
-// A matching fingerprint is confirmed by comparing the n tokens in the
-// history, so a fingerprint collision only costs another probe. Tables have
-// at least twice as many slots as max_len, so a free slot always exists and
-// a probe sequence always ends. Entries are never removed (positions only
-// grow) except when the whole store is reset.
+// An insert walks the probe sequence of its hash to the first slot that is
+// empty (claimed with a compare-and-swap) or holds its fingerprint, and
+// keeps the larger end there with a 64-bit atomicMax (the fingerprint half
+// is the same). Slots are never emptied and never change fingerprint, so
+// for each fingerprint that first slot is fixed, every n-gram with that
+// fingerprint merges into it, and the slot holds the largest end over all of
+// them. A query walks the same sequence: an empty slot first means the
+// n-gram was never inserted; otherwise the stored end is confirmed against
+// the history's tokens, and a confirmed end is the n-gram's most recent
+// occurrence (it is the largest end of all n-grams merged there). An end
+// that does not confirm means two n-grams share a fingerprint; the request
+// is then answered by an exact scan of its history. Tables have at least
+// twice as many slots as max_len, so a free slot always exists and every
+// probe sequence ends.
 //
-// pld_index_insert runs before the append's copy: for every end position
-// that the append makes draftable (old L - 1 .. new L - 2) it inserts the
-// n-grams ending there, reading old tokens from the store and new ones from
-// the append's source buffer. Concurrent inserts of one n-gram claim a slot
-// with a compare-and-swap and keep the largest position with a 64-bit
-// atomicMax (the fingerprint half of the word is the same).
+// Inserts run before the append's copy: for every end position that the
+// append makes draftable (old L - 1 .. new L - 2) the n-grams ending there
+// are inserted, old tokens read from the store and new ones from the
+// append's source rows.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -64,6 +71,10 @@ __device__ __forceinline__ u64 hfinal(u64 h)
 
 constexpr u64 kHashSeed = 0x243f6a8885a308d3ull;
 
+// LDS tokens for the n-grams of a one-workgroup append (appends up to 1,024
+// tokens plus the 63 before them; longer ones hash from memory).
+constexpr int kAppendWindow = 1024 + 64;
+
 __device__ __forceinline__ u64 *table_of(const IndexArgs &a, int b, int n)
 {
     return a.table + ((int64_t)b * (a.n_hi - a.n_lo + 1) + (n - a.n_lo)) * a.cap;
@@ -77,45 +88,80 @@ struct AppendView {
     int32_t old_len;
     __device__ __forceinline__ int32_t at(int64_t q) const
     {
-        return q < old_len ? store_row[q] : src[q - old_len];
+        // one load from whichever buffer holds q
+        const int32_t *p = q < old_len ? store_row + q : src + (q - old_len);
+        return *p;
     }
 };
 
-__device__ __forceinline__ bool same_gram(const AppendView &v, int64_t p, int64_t q, int n)
+// Inserts the end e of an n-gram with hash f into its table: into the
+// first slot of the probe sequence that is empty or holds the fingerprint.
+__device__ void insert_gram(u64 *tab, int64_t cap, uint32_t fp_mask, int64_t e, u64 f)
 {
-    for (int i = 0; i < n; ++i)
-        if (v.at(p - i) != v.at(q - i))
-            return false;
-    return true;
-}
-
-// Inserts the n-gram ending at e (hash f) into its table, keeping the
-// largest end position per n-gram.
-__device__ void insert_gram(u64 *tab, int64_t cap, const AppendView &v, int64_t e, int n, u64 f)
-{
-    const uint32_t fp = (uint32_t)(f >> 32);
+    const uint32_t fp = (uint32_t)(f >> 32) & fp_mask;
     const u64 word = ((u64)fp << 32) | (uint32_t)(e + 1);
     int64_t slot = (int64_t)(f & (u64)(cap - 1));
     for (int64_t probe = 0; probe < cap; ++probe) {
-        u64 cur = __hip_atomic_load(tab + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (cur == 0) {
-            u64 expected = 0;
-            if (__hip_atomic_compare_exchange_strong(tab + slot, &expected, word, __ATOMIC_RELAXED,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-                return;
-            cur = expected;  // another insert claimed the slot first
-        }
+        // claim an empty slot; a failed claim returns what the slot holds
+        u64 cur = 0;
+        if (__hip_atomic_compare_exchange_strong(tab + slot, &cur, word, __ATOMIC_RELAXED,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            return;
         if ((uint32_t)(cur >> 32) == fp) {
-            const int64_t q = (int64_t)(uint32_t)cur - 1;
-            if (same_gram(v, e, q, n)) {
-                __hip_atomic_fetch_max(tab + slot, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                return;
-            }
+            __hip_atomic_fetch_max(tab + slot, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
         }
         slot = (slot + 1) & (cap - 1);
     }
 }
 
+// Inserts the (end, length) pairs p0, p0 + step, ... of one append:
+// pairs are numbered end-major over ends e_first..new_len-2 and lengths
+// n_lo..n_hi, so the threads of a workgroup take neighbouring lengths of the
+// same ends and every pair costs one hash of n tokens and one probe sequence.
+// The tokens are read through `tok(q)` (LDS or memory).
+template <typename Tok>
+__device__ __forceinline__ void insert_pairs(const IndexArgs &a, int b, const AppendView &v,
+                                             int64_t new_len, int64_t p0, int64_t step,
+                                             const Tok &tok)
+{
+    const int64_t e_first = v.old_len > 0 ? v.old_len - 1 : 0;
+    if (new_len - 2 < e_first)
+        return;
+    const int nl = a.n_hi - a.n_lo + 1;
+    const int64_t pairs = (new_len - 2 - e_first + 1) * nl;
+    for (int64_t p = p0; p < pairs; p += step) {
+        const int64_t e = e_first + p / nl;
+        const int n = a.n_lo + (int)(p % nl);
+        if (e - n + 1 < 0)
+            continue;
+        u64 h = kHashSeed;
+        for (int i = 0; i < n; ++i)
+            h = hstep(h, tok(e - i));
+        insert_gram(table_of(a, b, n), a.cap, a.fp_mask, e, hfinal(h));
+    }
+}
+
+struct MemTok {
+    const AppendView *v;
+    __device__ __forceinline__ int32_t operator()(int64_t q) const { return v->at(q); }
+};
+
+// Tokens q0 .. q0 + n - 1 of the request staged in LDS.
+struct LdsTok {
+    const int32_t *w;
+    int64_t q0;
+    __device__ __forceinline__ int32_t operator()(int64_t q) const { return w[q - q0]; }
+};
+
+// The checks pld_append_kernel makes, in the same words.
+__device__ __forceinline__ bool append_ok(const IndexArgs &a, int32_t old_len, int32_t c)
+{
+    return c >= 0 && old_len >= 0 && (int64_t)old_len + c <= a.max_len;
+}
+
+// Inserts of an append spread over several workgroups per request (large
+// appends); pld_append_kernel copies the tokens afterwards.
 __global__ __launch_bounds__(256) void pld_index_insert(IndexArgs a, const int32_t *tokens,
                                                         int64_t tokens_stride,
                                                         const int32_t *counts)
@@ -123,31 +169,116 @@ __global__ __launch_bounds__(256) void pld_index_insert(IndexArgs a, const int32
     const int b = blockIdx.x;
     const int32_t old_len = a.lengths[b];
     const int32_t c = counts[b];
-    // an append the copy kernel will reject inserts nothing
-    if (c <= 0 || old_len < 0 || (int64_t)old_len + c > a.max_len)
-        return;
-    const int64_t new_len = (int64_t)old_len + c;
+    if (c <= 0 || !append_ok(a, old_len, c))
+        return;  // nothing to insert, or the copy kernel rejects the append
     AppendView v{a.store + (int64_t)b * a.pitch, tokens + (int64_t)b * tokens_stride, old_len};
+    insert_pairs(a, b, v, (int64_t)old_len + c,
+                 (int64_t)blockIdx.y * blockDim.x + threadIdx.x, (int64_t)gridDim.y * blockDim.x,
+                 MemTok{&v});
+}
+
+// A whole append of one request in one workgroup (small appends, as in a
+// decode loop): inserts, copy, then the new length. The inserts read new
+// tokens from the source row, so they do not depend on the copy.
+__global__ __launch_bounds__(256) void pld_append_indexed(IndexArgs a, const int32_t *tokens,
+                                                          int64_t tokens_stride,
+                                                          const int32_t *counts)
+{
+    __shared__ int s_ok;
+    __shared__ int32_t win[kAppendWindow];
+    const int b = blockIdx.x;
+    const int32_t old_len = a.lengths[b];
+    const int32_t c = counts[b];
+    if (threadIdx.x == 0) {
+        const bool ok = append_ok(a, old_len, c);
+        if (!ok)
+            atomicOr(a.err, c < 0 ? kErrAppendNegative : kErrAppendCapacity);
+        s_ok = ok;
+    }
+    __syncthreads();
+    if (!s_ok || c == 0)
+        return;
+    int32_t *row = a.store + (int64_t)b * a.pitch;
+    const int32_t *src = tokens + (int64_t)b * tokens_stride;
+    AppendView v{row, src, old_len};
+    const int64_t new_len = (int64_t)old_len + c;
+    // the tokens the new n-grams span: from n_hi - 1 before the first new
+    // end to the last new end
     const int64_t e_first = old_len > 0 ? old_len - 1 : 0;
-    const int64_t step = (int64_t)gridDim.y * blockDim.x;
-    for (int64_t e = e_first + (int64_t)blockIdx.y * blockDim.x + threadIdx.x; e <= new_len - 2;
-         e += step) {
-        u64 h = kHashSeed;
-        for (int n = 1; n <= a.n_hi && e - n + 1 >= 0; ++n) {
-            h = hstep(h, v.at(e - n + 1));
-            if (n >= a.n_lo)
-                insert_gram(table_of(a, b, n), a.cap, v, e, n, hfinal(h));
+    const int64_t q0 = e_first - (a.n_hi - 1) > 0 ? e_first - (a.n_hi - 1) : 0;
+    const int64_t nw = new_len - 1 - q0;
+    if (nw <= kAppendWindow) {
+        for (int64_t i = threadIdx.x; i < nw; i += blockDim.x)
+            win[i] = v.at(q0 + i);
+        __syncthreads();
+        insert_pairs(a, b, v, new_len, threadIdx.x, blockDim.x, LdsTok{win, q0});
+    } else {
+        insert_pairs(a, b, v, new_len, threadIdx.x, blockDim.x, MemTok{&v});
+    }
+    for (int32_t t = threadIdx.x; t < c; t += blockDim.x)
+        row[old_len + t] = src[t];
+    __syncthreads();
+    if (threadIdx.x == 0)
+        a.lengths[b] = old_len + c;
+}
+
+// Walks the probe sequence of hash f in the table of one length: the end
+// stored in the first slot that holds the fingerprint, or -1 when an empty
+// slot comes first (the n-gram was never inserted).
+__device__ __forceinline__ int64_t probe_fp(const u64 *tab, int64_t cap, uint32_t fp_mask, u64 f)
+{
+    const uint32_t fp = (uint32_t)(f >> 32) & fp_mask;
+    int64_t slot = (int64_t)(f & (u64)(cap - 1));
+    for (int64_t probe = 0; probe < cap; ++probe) {
+        const u64 cur = tab[slot];
+        if (cur == 0)
+            break;
+        if ((uint32_t)(cur >> 32) == fp)
+            return (int64_t)(uint32_t)cur - 1;
+        slot = (slot + 1) & (cap - 1);
+    }
+    return -1;
+}
+
+__device__ __forceinline__ u64 wave_max(u64 key)
+{
+    for (int off = 32; off >= 1; off >>= 1) {
+        const u64 o = __shfl_xor(key, off);
+        key = o > key ? o : key;
+    }
+    return key;
+}
+
+// The exact answer by a scan of the row (only after a fingerprint
+// collision): the maximum over end positions e <= L - 2 of
+// (l(e) << 32 | e), l(e) the backward agreement with the suffix capped at
+// mhat, counted when l(e) >= n_min.
+__device__ u64 scan_row(const int32_t *row, int32_t L, int32_t mhat, int32_t n_min,
+                        const int32_t *suf, int lane)
+{
+    u64 best = 0;
+    for (int64_t e = lane; e <= (int64_t)L - 2; e += kWave) {
+        int32_t l = 0;
+        while (l < mhat && e - l >= 0 && row[e - l] == suf[l])
+            ++l;
+        if (l >= n_min) {
+            const u64 k = ((u64)(uint32_t)l << 32) | (uint32_t)e;
+            best = k > best ? k : best;
         }
     }
+    return wave_max(best);
 }
 
 // One wavefront per request: lane i holds suffix token L - 1 - i, lane
-// n - 1 probes the table of length n.
+// n - 1 probes the table of length n. The longest length whose suffix
+// n-gram is in the index is confirmed against the stored tokens in the same
+// round trip that loads its draft tokens.
 __global__ __launch_bounds__(kWave) void pld_index_draft(IndexArgs a, int32_t n_min, int32_t n_max,
                                                          int32_t k_max, int32_t *out_draft,
                                                          int32_t *out_len, int32_t *out_match,
                                                          int32_t *out_pos)
 {
+    __shared__ int32_t suf[kWave];
     const int b = blockIdx.x;
     const int lane = threadIdx.x;
     const int32_t len = a.lengths[b];
@@ -166,34 +297,11 @@ __global__ __launch_bounds__(kWave) void pld_index_draft(IndexArgs a, int32_t n_
             mine = h;
     }
     const int n = lane + 1;
-    u64 key = 0;
-    if (n >= n_min && n <= mhat) {
-        const u64 f = hfinal(mine);
-        const uint32_t fp = (uint32_t)(f >> 32);
-        const u64 *tab = table_of(a, b, n);
-        int64_t slot = (int64_t)(f & (u64)(a.cap - 1));
-        for (int64_t probe = 0; probe < a.cap; ++probe) {
-            const u64 cur = tab[slot];
-            if (cur == 0)
-                break;
-            if ((uint32_t)(cur >> 32) == fp) {
-                const int64_t q = (int64_t)(uint32_t)cur - 1;
-                bool same = q <= L - 2 && q - n + 1 >= 0;
-                for (int i = 0; same && i < n; ++i)
-                    same = row[q - i] == row[L - 1 - i];
-                if (same) {
-                    key = ((u64)(uint32_t)n << 32) | (uint32_t)q;
-                    break;
-                }
-            }
-            slot = (slot + 1) & (a.cap - 1);
-        }
-    }
-    // longest length, then (the one position kept for it) the key's end
-    for (int off = 32; off >= 1; off >>= 1) {
-        const u64 o = __shfl_xor(key, off);
-        key = o > key ? o : key;
-    }
+    int64_t q = -1;
+    if (n >= n_min && n <= mhat)
+        q = probe_fp(table_of(a, b, n), a.cap, a.fp_mask, hfinal(mine));
+    u64 key = wave_max(q >= 0 ? ((u64)(uint32_t)n << 32) | (uint32_t)q : 0);
+
     int32_t m = 0, d = 0, e = -1;
     if (key != 0) {
         m = (int32_t)(key >> 32);
@@ -201,8 +309,29 @@ __global__ __launch_bounds__(kWave) void pld_index_draft(IndexArgs a, int32_t n_
         const int32_t follow = L - 1 - e;
         d = follow < k_max ? follow : k_max;
     }
+    // confirm the end (lane i < m: token e - i) and load the draft tokens
+    // (lane t < d) in one round trip
+    const bool in_range = key != 0 && e <= L - 2 && e - m + 1 >= 0;
+    const bool agree = !(in_range && lane < m) || row[e - lane] == tok;
+    int32_t cont = in_range && lane < d ? row[(int64_t)e + 1 + lane] : -1;
+    if (key != 0 && !(in_range && __all(agree))) {
+        // two n-grams share a fingerprint: answer by scanning the row
+        suf[lane] = tok;
+        __syncthreads();
+        key = scan_row(row, L, mhat, n_min, suf, lane);
+        m = 0, d = 0, e = -1;
+        if (key != 0) {
+            m = (int32_t)(key >> 32);
+            e = (int32_t)(key & 0xffffffffu);
+            const int32_t follow = L - 1 - e;
+            d = follow < k_max ? follow : k_max;
+        }
+        cont = lane < d ? row[(int64_t)e + 1 + lane] : -1;
+    }
     int32_t *orow = out_draft + (int64_t)b * k_max;
-    for (int t = lane; t < k_max; t += kWave)
+    if (lane < k_max)
+        orow[lane] = cont;
+    for (int t = lane + kWave; t < k_max; t += kWave)
         orow[t] = t < d ? row[(int64_t)e + 1 + t] : -1;
     if (lane == 0) {
         out_len[b] = d;
@@ -229,6 +358,17 @@ hipError_t launch_index_insert(const IndexArgs &a, const int32_t *tokens, int64_
         return hipSuccess;
     hipLaunchKernelGGL(pld_index_insert, dim3((unsigned)batch, (unsigned)chunks), dim3(256), 0, s,
                        a, tokens, tokens_stride, counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_indexed(const IndexArgs &a, const int32_t *tokens,
+                                 int64_t tokens_stride, const int32_t *counts, int32_t batch,
+                                 hipStream_t s)
+{
+    if (batch <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(pld_append_indexed, dim3((unsigned)batch), dim3(256), 0, s, a, tokens,
+                       tokens_stride, counts);
     return hipGetLastError();
 }
 

@@ -93,6 +93,7 @@ struct IndexArgs {
     int64_t pitch;
     int32_t *lengths;           // [max_batch]
     int32_t max_len;
+    uint32_t fp_mask;           // fingerprint bits kept (all 32 but in tests)
     unsigned int *err;
 };
 
@@ -106,6 +107,9 @@ hipError_t launch_fuse(const FuseArgs &a, int32_t batch, hipStream_t s);
 hipError_t launch_index_insert(const IndexArgs &a, const int32_t *tokens, int64_t tokens_stride,
                                const int32_t *counts, int32_t batch, int32_t chunks,
                                hipStream_t s);
+hipError_t launch_append_indexed(const IndexArgs &a, const int32_t *tokens,
+                                 int64_t tokens_stride, const int32_t *counts, int32_t batch,
+                                 hipStream_t s);
 hipError_t launch_index_draft(const IndexArgs &a, int32_t batch, int32_t n_min, int32_t n_max,
                               int32_t k_max, int32_t *out_draft, int32_t *out_len,
                               int32_t *out_match, int32_t *out_pos, hipStream_t s);

@@ -228,3 +228,37 @@ def test_index_agrees_with_scan_on_store():
             assert np.array_equal(x, y)
     finally:
         s.close()
+
+
+@pytest.mark.parametrize("bits", [0, 3, 12])
+def test_index_fingerprint_collisions(bits):
+    """With few fingerprint bits, n-grams share slots all the time and most
+    queries land on a slot that does not confirm: those requests are answered
+    by the exact scan, and every result still equals the oracle's."""
+    rng = np.random.default_rng([9004, bits])
+    s = IndexedStore(5, 3000, 3, 9)
+    try:
+        B.pld_index_fingerprint_bits(s.ctx, bits)
+        s.append([rng.integers(0, 6, int(rng.integers(50, 1500))).astype(np.int32)
+                  for _ in range(5)])
+        for step in range(12):
+            s.check(3, 9, 12, f"bits {bits} step {step}")
+            rows = []
+            for b in range(5):
+                c = min(3000 - len(s.host[b]), int(rng.integers(0, 60)))
+                if rng.random() < 0.4 and len(s.host[b]) > 20:
+                    start = int(rng.integers(0, len(s.host[b]) - 20))
+                    r = s.host[b][start:start + c]
+                else:
+                    r = rng.integers(0, 6, c)
+                rows.append(np.asarray(r, np.int32))
+            s.append(rows)
+        s.check(4, 6, 5, f"bits {bits} final")
+    finally:
+        s.close()
+    with pytest.raises(B.PldError):
+        plain = B.pld_create(1, 10, own_store=True)
+        try:
+            B.pld_index_fingerprint_bits(plain, 8)
+        finally:
+            B.pld_destroy(plain)
