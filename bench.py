@@ -93,6 +93,12 @@ def parse():
     ap.add_argument("--index", action="store_true",
                     help="workload 5 only: draft from the context's incremental n-gram "
                          "index (pld_create_indexed, pld_draft_store) instead of scanning")
+    ap.add_argument("--stream-start", type=int, default=0,
+                    help="workload 5 only: start histories of this many tokens instead "
+                         "of 32,768 (the same decode on longer histories)")
+    ap.add_argument("--append-draft", action="store_true",
+                    help="workload 5 only: each step's append and the next step's draft "
+                         "as one pld_append_draft_store call")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with 8 plain 64 MiB device copies (a counter "
                          "reference of known size for rocprofv3 --pmc)")
@@ -474,12 +480,14 @@ def bench_stream(args, torch, B, wl, dev):
     previous draft while it lasts, then fresh Zipf tokens; they are fixed
     by one untimed closed-loop pass, then all 1,024 steps are captured in a
     HIP graph and replayed from the same start state."""
-    start = wl.config5_start()
+    start_len = args.stream_start or wl.STREAM_START_LEN
+    start = wl.config5_start(start_len)
     nb, steps_n, width = start.batch, wl.STREAM_STEPS, wl.STREAM_MAX_APPEND
+    max_len = start_len + steps_n * width
     if args.index:
-        ctx = B.pld_create_indexed(nb, wl.STREAM_MAX_LEN, start.n_min, start.n_max)
+        ctx = B.pld_create_indexed(nb, max_len, start.n_min, start.n_max)
     else:
-        ctx = B.pld_create(nb, wl.STREAM_MAX_LEN, own_store=True)
+        ctx = B.pld_create(nb, max_len, own_store=True)
     rows, lens = B.pld_store_views(ctx)
 
     def draft():
@@ -490,19 +498,19 @@ def bench_stream(args, torch, B, wl, dev):
             B.pld_draft_batch(ctx, rows, lens, nb, start.n_min, start.n_max, start.k_max,
                               out[0], out[1], out[2])
     init = torch.from_numpy(np.stack(start.histories)).to(dev)
-    init_counts = torch.full((nb,), wl.STREAM_START_LEN, dtype=torch.int32, device=dev)
+    init_counts = torch.full((nb,), start_len, dtype=torch.int32, device=dev)
     out = B.alloc_outputs(nb, start.k_max, device=dev)
 
     def restart():
         B.pld_store_reset(ctx)
-        B.pld_append(ctx, init, wl.STREAM_START_LEN, init_counts, nb)
+        B.pld_append(ctx, init, start_len, init_counts, nb)
 
     # untimed closed loop: fixes the append stream from the GPU's drafts
     restart()
     toks = np.zeros((steps_n, nb, width), np.int32)
     cnts = np.zeros((steps_n, nb), np.int32)
     first_drafts = []  # every step's drafts, for the oracle comparison
-    lengths = np.full(nb, wl.STREAM_START_LEN, np.int64)
+    lengths = np.full(nb, start_len, np.int64)
     total_tokens = 0
     for step in range(steps_n):
         draft()
@@ -527,9 +535,18 @@ def bench_stream(args, torch, B, wl, dev):
     restart()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph, stream=cap):
-        for step in range(steps_n):
+        if args.append_draft:
+            # draft(0), then append(s) + draft(s + 1) per call, then the last append
             draft()
-            B.pld_append(ctx, toks_d[step], width, cnts_d[step], nb)
+            for step in range(steps_n - 1):
+                B.pld_append_draft_store(ctx, toks_d[step], width, cnts_d[step], nb,
+                                         start.n_min, start.n_max, start.k_max, out[0], out[1],
+                                         out[2])
+            B.pld_append(ctx, toks_d[steps_n - 1], width, cnts_d[steps_n - 1], nb)
+        else:
+            for step in range(steps_n):
+                draft()
+                B.pld_append(ctx, toks_d[step], width, cnts_d[step], nb)
     times = []
     reps = max(1, args.steps // steps_n) if args.steps >= steps_n else 1
     for rep in range(reps + 1):  # the first replay is warm-up
@@ -565,10 +582,11 @@ def bench_stream(args, torch, B, wl, dev):
         "vs_baseline": None,
         "dtype": "int32",
         "data": "synthetic",
-        "config": {"workload": start.name, "batch": nb, "start_tokens": wl.STREAM_START_LEN,
+        "config": {"workload": start.name, "batch": nb, "start_tokens": start_len,
                    "steps": steps_n, "n_min": start.n_min, "n_max": start.n_max,
                    "k_max": start.k_max, "mean_bytes_per_step": round(bytes_mean),
-                   "drafting": "n-gram index" if args.index else "scan"},
+                   "drafting": "n-gram index" if args.index else "scan",
+                   "calls_per_step": 1 if args.append_draft else 2},
         "us_per_step_append_plus_draft": round(gpu_s * 1e6 / steps_n, 3),
         # for the index: the history bytes a scan would have read, per second
         ("scan_equivalent_GBps" if args.index else "scan_GBps"):

@@ -233,6 +233,25 @@ pld_status pld_draft_store(pld_ctx *ctx, int32_t batch, int32_t n_min, int32_t n
                            int32_t *out_match, int32_t *out_pos, hipStream_t stream);
 
 /*
+ * One decode step on the context's store: pld_append (tokens, tokens_stride,
+ * counts, batch as there), then the draft of the first `batch` rows of the
+ * new histories (n_min, n_max, k_max and outputs as in pld_draft_store or,
+ * without an index, pld_draft_batch_pos on pld_store_views; out_pos may be
+ * NULL). On an indexed context n_min, n_max must lie inside the indexed
+ * lengths; with 0 < tokens_stride <= 1024 both steps then run in one launch
+ * (one workgroup per request), otherwise as two calls. Results are the same
+ * either way. A rejected append (see pld_append) leaves its row as it was,
+ * and that row is drafted as it stands. All arguments are checked before
+ * anything is enqueued.
+ * Errors: those of pld_append and of the draft call.
+ */
+pld_status pld_append_draft_store(pld_ctx *ctx, const int32_t *tokens, int64_t tokens_stride,
+                                  const int32_t *counts, int32_t batch, int32_t n_min,
+                                  int32_t n_max, int32_t k_max, int32_t *out_draft,
+                                  int32_t *out_len, int32_t *out_match, int32_t *out_pos,
+                                  hipStream_t stream);
+
+/*
  * Draft fusion and long-block scheduling (HyperQwen lookup-drafting page,
  * "lookup drafting: the three-step principle", steps 2 and 3).
  *

@@ -30,7 +30,7 @@ PLD_FUSE_MAX_POSITIONS = 64
 EXPORTS = ("pld_create", "pld_create_indexed", "pld_destroy", "pld_configure", "pld_append",
            "pld_store_views", "pld_store_reset", "pld_draft_batch",
            "pld_draft_batch_pos", "pld_draft_batch_strided", "pld_index_fingerprint_bits",
-           "pld_draft_store",
+           "pld_draft_store", "pld_append_draft_store",
            "pld_fuse_params_default",
            "pld_fuse", "pld_draft_fuse_batch", "pld_sync", "pld_strerror",
            "pld_last_error")
@@ -75,6 +75,7 @@ def load(path: str = LIB_PATH):
         "pld_draft_batch_strided": [vp, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp,
                                     vp, vp],
         "pld_index_fingerprint_bits": [vp, i32],
+        "pld_append_draft_store": [vp, vp, i64, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp],
         "pld_draft_store": [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp],
         "pld_fuse_params_default": [ctypes.POINTER(PldFuseParams)],
         "pld_fuse": [vp, ctypes.POINTER(PldFuseParams), vp, i32, vp, vp, vp, vp, vp, i32,
@@ -230,6 +231,19 @@ def pld_draft_batch_strided(ctx: int, base, stride: int, lengths, min_len: int,
     _check("pld_draft_batch_strided", load().pld_draft_batch_strided(
         ctx, _dev_ptr(base, "base", i32), int(stride), _dev_ptr(lengths, "lengths", i32),
         int(min_len), int(batch), int(n_min), int(n_max), int(k_max),
+        _dev_ptr(out_draft, "out_draft", i32), _dev_ptr(out_len, "out_len", i32),
+        _dev_ptr(out_match, "out_match", i32), _dev_ptr(out_pos, "out_pos", i32),
+        _stream(stream)))
+
+
+def pld_append_draft_store(ctx: int, tokens, tokens_stride: int, counts, batch: int,
+                           n_min: int, n_max: int, k_max: int, out_draft, out_len, out_match,
+                           out_pos=None, stream=None) -> None:
+    """pld_append, then draft the store's first `batch` rows (include/pld.h)."""
+    i32 = _i32()
+    _check("pld_append_draft_store", load().pld_append_draft_store(
+        ctx, _dev_ptr(tokens, "tokens", i32), int(tokens_stride),
+        _dev_ptr(counts, "counts", i32), int(batch), int(n_min), int(n_max), int(k_max),
         _dev_ptr(out_draft, "out_draft", i32), _dev_ptr(out_len, "out_len", i32),
         _dev_ptr(out_match, "out_match", i32), _dev_ptr(out_pos, "out_pos", i32),
         _stream(stream)))

@@ -439,6 +439,55 @@ pld_status pld_store_reset(pld_ctx *ctx, hipStream_t stream)
     return PLD_OK;
 }
 
+pld_status pld_append_draft_store(pld_ctx *ctx, const int32_t *tokens, int64_t tokens_stride,
+                                  const int32_t *counts, int32_t batch, int32_t n_min,
+                                  int32_t n_max, int32_t k_max, int32_t *out_draft,
+                                  int32_t *out_len, int32_t *out_match, int32_t *out_pos,
+                                  hipStream_t stream)
+{
+    if (!ctx)
+        return fail(PLD_EINVAL, "ctx is null");
+    if (!ctx->store)
+        return fail(PLD_EINVAL, "context was created without a store");
+    // every draft argument is checked before the append is enqueued
+    const int32_t lo = ctx->index ? ctx->index_lo : 1;
+    const int32_t hi = ctx->index ? ctx->index_hi : PLD_N_MAX_LIMIT;
+    if (n_min < lo || n_max < n_min || n_max > hi)
+        return fail(PLD_EINVAL, "need %d <= n_min <= n_max <= %d (got n_min=%d n_max=%d)", lo,
+                    hi, n_min, n_max);
+    if (k_max < 1)
+        return fail(PLD_EINVAL, "k_max must be >= 1 (got %d)", k_max);
+    if (batch < 0 || batch > ctx->max_batch)
+        return fail(PLD_EINVAL, "batch %d outside [0, max_batch=%d]", batch, ctx->max_batch);
+    if (batch > 0 && (!out_draft || !out_len || !out_match))
+        return fail(PLD_EINVAL, "null buffer pointer");
+    const bool fused = ctx->index && tokens_stride > 0 && tokens_stride <= kSmallAppend;
+    if (!fused) {
+        // the same two steps, one after the other on the stream
+        pld_status st = pld_append(ctx, tokens, tokens_stride, counts, batch, stream);
+        if (st != PLD_OK)
+            return st;
+        if (ctx->index)
+            return pld_draft_store(ctx, batch, n_min, n_max, k_max, out_draft, out_len,
+                                   out_match, out_pos, stream);
+        return draft(ctx, ctx->store_rows, nullptr, 0, 0, ctx->store_len, batch, n_min, n_max,
+                     k_max, out_draft, out_len, out_match, out_pos, stream);
+    }
+    if (batch == 0)
+        return PLD_OK;
+    if (!tokens || !counts)
+        return fail(PLD_EINVAL, "null buffer pointer");
+    if (((uintptr_t)tokens | (uintptr_t)counts | (uintptr_t)out_draft | (uintptr_t)out_len |
+         (uintptr_t)out_match | (uintptr_t)out_pos) & 3u)
+        return fail(PLD_EINVAL, "buffers must be 4-byte aligned");
+    hipError_t e = pld::launch_append_draft_indexed(index_args(ctx), tokens, tokens_stride, counts,
+                                                    batch, n_min, n_max, k_max, out_draft,
+                                                    out_len, out_match, out_pos, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "append-draft launch");
+    return PLD_OK;
+}
+
 pld_status pld_index_fingerprint_bits(pld_ctx *ctx, int32_t bits)
 {
     if (!ctx)

@@ -224,13 +224,17 @@ __global__ __launch_bounds__(256) void pld_append_indexed(IndexArgs a, const int
 
 // Walks the probe sequence of hash f in the table of one length: the end
 // stored in the first slot that holds the fingerprint, or -1 when an empty
-// slot comes first (the n-gram was never inserted).
+// slot comes first (the n-gram was never inserted). COHERENT reads the
+// slots with agent-scope atomic loads (after this kernel's own inserts).
+template <bool COHERENT>
 __device__ __forceinline__ int64_t probe_fp(const u64 *tab, int64_t cap, uint32_t fp_mask, u64 f)
 {
     const uint32_t fp = (uint32_t)(f >> 32) & fp_mask;
     int64_t slot = (int64_t)(f & (u64)(cap - 1));
     for (int64_t probe = 0; probe < cap; ++probe) {
-        const u64 cur = tab[slot];
+        const u64 cur = COHERENT ? __hip_atomic_load(tab + slot, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)
+                                 : tab[slot];
         if (cur == 0)
             break;
         if ((uint32_t)(cur >> 32) == fp)
@@ -249,17 +253,23 @@ __device__ __forceinline__ u64 wave_max(u64 key)
     return key;
 }
 
-// The exact answer by a scan of the row (only after a fingerprint
+struct RowTok {
+    const int32_t *row;
+    __device__ __forceinline__ int32_t operator()(int64_t q) const { return row[q]; }
+};
+
+// The exact answer by a scan of the history (only after a fingerprint
 // collision): the maximum over end positions e <= L - 2 of
 // (l(e) << 32 | e), l(e) the backward agreement with the suffix capped at
 // mhat, counted when l(e) >= n_min.
-__device__ u64 scan_row(const int32_t *row, int32_t L, int32_t mhat, int32_t n_min,
+template <typename Tok>
+__device__ u64 scan_row(const Tok &tok_at, int32_t L, int32_t mhat, int32_t n_min,
                         const int32_t *suf, int lane)
 {
     u64 best = 0;
     for (int64_t e = lane; e <= (int64_t)L - 2; e += kWave) {
         int32_t l = 0;
-        while (l < mhat && e - l >= 0 && row[e - l] == suf[l])
+        while (l < mhat && e - l >= 0 && tok_at(e - l) == suf[l])
             ++l;
         if (l >= n_min) {
             const u64 k = ((u64)(uint32_t)l << 32) | (uint32_t)e;
@@ -269,26 +279,18 @@ __device__ u64 scan_row(const int32_t *row, int32_t L, int32_t mhat, int32_t n_m
     return wave_max(best);
 }
 
-// One wavefront per request: lane i holds suffix token L - 1 - i, lane
-// n - 1 probes the table of length n. The longest length whose suffix
-// n-gram is in the index is confirmed against the stored tokens in the same
-// round trip that loads its draft tokens.
-__global__ __launch_bounds__(kWave) void pld_index_draft(IndexArgs a, int32_t n_min, int32_t n_max,
-                                                         int32_t k_max, int32_t *out_draft,
-                                                         int32_t *out_len, int32_t *out_match,
-                                                         int32_t *out_pos)
+// The draft of request b (history of length L read through tok_at) from the
+// index, written to the outputs by one wavefront: lane i holds suffix token
+// L - 1 - i, lane n - 1 probes the table of length n. The longest length
+// whose suffix n-gram is in the index is confirmed against the history in
+// the same round trip that loads its draft tokens. `suf` is 64 ints of LDS.
+template <bool COHERENT, typename Tok>
+__device__ void index_query(const IndexArgs &a, int b, int lane, int32_t L, const Tok &tok_at,
+                            int32_t n_min, int32_t n_max, int32_t k_max, int32_t *out_draft,
+                            int32_t *out_len, int32_t *out_match, int32_t *out_pos, int32_t *suf)
 {
-    __shared__ int32_t suf[kWave];
-    const int b = blockIdx.x;
-    const int lane = threadIdx.x;
-    const int32_t len = a.lengths[b];
-    const int32_t L = len >= 0 && len <= a.max_len ? len : 0;
-    if (lane == 0 && L != len)
-        atomicOr(a.err, len < 0 ? kErrLenNegative : kErrLenCapacity);
-    const int32_t *row = a.store + (int64_t)b * a.pitch;
     const int32_t mhat = L - 1 < n_max ? L - 1 : n_max;
-
-    const int32_t tok = lane < mhat ? row[L - 1 - lane] : 0;
+    const int32_t tok = lane < mhat ? tok_at(L - 1 - lane) : 0;
     // hash of the suffix n-gram for n = lane + 1, built token by token
     u64 h = kHashSeed, mine = 0;
     for (int i = 0; i < mhat; ++i) {
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(kWave) void pld_index_draft(IndexArgs a, int32_t n_
     const int n = lane + 1;
     int64_t q = -1;
     if (n >= n_min && n <= mhat)
-        q = probe_fp(table_of(a, b, n), a.cap, a.fp_mask, hfinal(mine));
+        q = probe_fp<COHERENT>(table_of(a, b, n), a.cap, a.fp_mask, hfinal(mine));
     u64 key = wave_max(q >= 0 ? ((u64)(uint32_t)n << 32) | (uint32_t)q : 0);
 
     int32_t m = 0, d = 0, e = -1;
@@ -312,13 +314,13 @@ __global__ __launch_bounds__(kWave) void pld_index_draft(IndexArgs a, int32_t n_
     // confirm the end (lane i < m: token e - i) and load the draft tokens
     // (lane t < d) in one round trip
     const bool in_range = key != 0 && e <= L - 2 && e - m + 1 >= 0;
-    const bool agree = !(in_range && lane < m) || row[e - lane] == tok;
-    int32_t cont = in_range && lane < d ? row[(int64_t)e + 1 + lane] : -1;
+    const bool agree = !(in_range && lane < m) || tok_at(e - lane) == tok;
+    int32_t cont = in_range && lane < d ? tok_at((int64_t)e + 1 + lane) : -1;
     if (key != 0 && !(in_range && __all(agree))) {
-        // two n-grams share a fingerprint: answer by scanning the row
+        // two n-grams share a fingerprint: answer by scanning the history
         suf[lane] = tok;
-        __syncthreads();
-        key = scan_row(row, L, mhat, n_min, suf, lane);
+        __builtin_amdgcn_wave_barrier();
+        key = scan_row(tok_at, L, mhat, n_min, suf, lane);
         m = 0, d = 0, e = -1;
         if (key != 0) {
             m = (int32_t)(key >> 32);
@@ -326,19 +328,91 @@ __global__ __launch_bounds__(kWave) void pld_index_draft(IndexArgs a, int32_t n_
             const int32_t follow = L - 1 - e;
             d = follow < k_max ? follow : k_max;
         }
-        cont = lane < d ? row[(int64_t)e + 1 + lane] : -1;
+        cont = lane < d ? tok_at((int64_t)e + 1 + lane) : -1;
     }
     int32_t *orow = out_draft + (int64_t)b * k_max;
     if (lane < k_max)
         orow[lane] = cont;
     for (int t = lane + kWave; t < k_max; t += kWave)
-        orow[t] = t < d ? row[(int64_t)e + 1 + t] : -1;
+        orow[t] = t < d ? tok_at((int64_t)e + 1 + t) : -1;
     if (lane == 0) {
         out_len[b] = d;
         out_match[b] = m;
         if (out_pos)
             out_pos[b] = key != 0 ? e - m + 1 : -1;
     }
+}
+
+// pld_draft_store: one wavefront per request, history from the store.
+__global__ __launch_bounds__(kWave) void pld_index_draft(IndexArgs a, int32_t n_min, int32_t n_max,
+                                                         int32_t k_max, int32_t *out_draft,
+                                                         int32_t *out_len, int32_t *out_match,
+                                                         int32_t *out_pos)
+{
+    __shared__ int32_t suf[kWave];
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x;
+    const int32_t len = a.lengths[b];
+    const int32_t L = len >= 0 && len <= a.max_len ? len : 0;
+    if (lane == 0 && L != len)
+        atomicOr(a.err, len < 0 ? kErrLenNegative : kErrLenCapacity);
+    index_query<false>(a, b, lane, L, RowTok{a.store + (int64_t)b * a.pitch}, n_min, n_max, k_max,
+                       out_draft, out_len, out_match, out_pos, suf);
+}
+
+// pld_append_draft_store on an indexed context, one workgroup per request:
+// the append's inserts, the copy, then (once every insert is performed) the
+// draft of the new history by the first wavefront, which reads new tokens
+// from the source rows, and finally the new length.
+__global__ __launch_bounds__(256) void pld_append_draft_indexed(
+    IndexArgs a, const int32_t *tokens, int64_t tokens_stride, const int32_t *counts,
+    int32_t n_min, int32_t n_max, int32_t k_max, int32_t *out_draft, int32_t *out_len,
+    int32_t *out_match, int32_t *out_pos)
+{
+    __shared__ int s_ok;
+    __shared__ int32_t win[kAppendWindow];
+    __shared__ int32_t suf[kWave];
+    const int b = blockIdx.x;
+    const int32_t old_len = a.lengths[b];
+    const int32_t c = counts[b];
+    if (threadIdx.x == 0) {
+        const bool ok = append_ok(a, old_len, c);
+        if (!ok)
+            atomicOr(a.err, c < 0 ? kErrAppendNegative : kErrAppendCapacity);
+        s_ok = ok;
+    }
+    __syncthreads();
+    // a rejected append leaves the history as it was; it is still drafted
+    const bool ok = s_ok;
+    const int32_t base_len = old_len >= 0 && old_len <= a.max_len ? old_len : 0;
+    const int32_t add = ok ? c : 0;
+    int32_t *row = a.store + (int64_t)b * a.pitch;
+    const int32_t *src = tokens + (int64_t)b * tokens_stride;
+    AppendView v{row, src, base_len};
+    const int64_t new_len = (int64_t)base_len + add;
+    if (add > 0) {
+        const int64_t e_first = base_len > 0 ? base_len - 1 : 0;
+        const int64_t q0 = e_first - (a.n_hi - 1) > 0 ? e_first - (a.n_hi - 1) : 0;
+        const int64_t nw = new_len - 1 - q0;
+        if (nw <= kAppendWindow) {
+            for (int64_t i = threadIdx.x; i < nw; i += blockDim.x)
+                win[i] = v.at(q0 + i);
+            __syncthreads();
+            insert_pairs(a, b, v, new_len, threadIdx.x, blockDim.x, LdsTok{win, q0});
+        } else {
+            insert_pairs(a, b, v, new_len, threadIdx.x, blockDim.x, MemTok{&v});
+        }
+        for (int32_t t = threadIdx.x; t < add; t += blockDim.x)
+            row[base_len + t] = src[t];
+    }
+    // every insert (and copy) performed before the first wavefront probes
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x < kWave)
+        index_query<true>(a, b, threadIdx.x, (int32_t)new_len, MemTok{&v}, n_min, n_max, k_max,
+                          out_draft, out_len, out_match, out_pos, suf);
+    if (threadIdx.x == 0 && add > 0)
+        a.lengths[b] = (int32_t)new_len;
 }
 
 __global__ __launch_bounds__(256) void pld_fill_u64(u64 *p, int64_t n)
@@ -369,6 +443,20 @@ hipError_t launch_append_indexed(const IndexArgs &a, const int32_t *tokens,
         return hipSuccess;
     hipLaunchKernelGGL(pld_append_indexed, dim3((unsigned)batch), dim3(256), 0, s, a, tokens,
                        tokens_stride, counts);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_draft_indexed(const IndexArgs &a, const int32_t *tokens,
+                                       int64_t tokens_stride, const int32_t *counts,
+                                       int32_t batch, int32_t n_min, int32_t n_max,
+                                       int32_t k_max, int32_t *out_draft, int32_t *out_len,
+                                       int32_t *out_match, int32_t *out_pos, hipStream_t s)
+{
+    if (batch <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(pld_append_draft_indexed, dim3((unsigned)batch), dim3(256), 0, s, a, tokens,
+                       tokens_stride, counts, n_min, n_max, k_max, out_draft, out_len, out_match,
+                       out_pos);
     return hipGetLastError();
 }
 

@@ -110,6 +110,11 @@ hipError_t launch_index_insert(const IndexArgs &a, const int32_t *tokens, int64_
 hipError_t launch_append_indexed(const IndexArgs &a, const int32_t *tokens,
                                  int64_t tokens_stride, const int32_t *counts, int32_t batch,
                                  hipStream_t s);
+hipError_t launch_append_draft_indexed(const IndexArgs &a, const int32_t *tokens,
+                                       int64_t tokens_stride, const int32_t *counts,
+                                       int32_t batch, int32_t n_min, int32_t n_max,
+                                       int32_t k_max, int32_t *out_draft, int32_t *out_len,
+                                       int32_t *out_match, int32_t *out_pos, hipStream_t s);
 hipError_t launch_index_draft(const IndexArgs &a, int32_t batch, int32_t n_min, int32_t n_max,
                               int32_t k_max, int32_t *out_draft, int32_t *out_len,
                               int32_t *out_match, int32_t *out_pos, hipStream_t s);

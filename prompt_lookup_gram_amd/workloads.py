@@ -202,13 +202,15 @@ STREAM_MAX_APPEND = 16
 STREAM_MAX_LEN = STREAM_START_LEN + STREAM_STEPS * STREAM_MAX_APPEND  # 49,152
 
 
-def config5_start() -> Workload:
-    """64 requests at 32,768 tokens (31,768 Zipf + 1,000-token copy tail,
-    q = 1%), the state a streaming decode starts from."""
-    hs = [_copy_heavy(5, b, STREAM_START_LEN, 1_000, 0.01)
+def config5_start(start_len: int = STREAM_START_LEN) -> Workload:
+    """64 requests at 32,768 tokens (start_len - 1,000 Zipf + 1,000-token copy
+    tail, q = 1%), the state a streaming decode starts from. Other start
+    lengths give the same decode on longer or shorter histories."""
+    hs = [_copy_heavy(5, b, start_len, 1_000, 0.01)
           for b in range(STREAM_BATCH)]
-    return Workload("c5_stream_b64_32k", hs, 4, 12, 16,
-                    "B=64 streaming decode from L=32768, 1024 steps of 1..16 "
+    name = "c5_stream_b64_32k" if start_len == STREAM_START_LEN else f"c5_stream_b64_{start_len}"
+    return Workload(name, hs, 4, 12, 16,
+                    f"B=64 streaming decode from L={start_len}, 1024 steps of 1..16 "
                     "appended tokens")
 
 

@@ -262,3 +262,80 @@ def test_index_fingerprint_collisions(bits):
             B.pld_index_fingerprint_bits(plain, 8)
         finally:
             B.pld_destroy(plain)
+
+
+# ---------------------------------------------------------------------------
+# pld_append_draft_store: one decode step (append, then draft) per call
+# ---------------------------------------------------------------------------
+
+
+def _stream_with_append_draft(ctx, steps, fp_bits=None):
+    """The streaming workload driven by pld_append_draft_store: each call
+    appends a step's tokens and drafts the new histories; every draft is
+    compared with the oracle on the mirrored histories."""
+    import torch
+    start = wl.config5_start()
+    nb = start.batch
+    if fp_bits is not None:
+        B.pld_index_fingerprint_bits(ctx, fp_bits)
+    host = [h.copy() for h in start.histories]
+    out = B.alloc_outputs(nb, start.k_max)
+    init = torch.from_numpy(np.stack(start.histories)).cuda()
+    counts0 = torch.full((nb,), wl.STREAM_START_LEN, dtype=torch.int32, device="cuda")
+    B.pld_append_draft_store(ctx, init, wl.STREAM_START_LEN, counts0, nb, start.n_min,
+                             start.n_max, start.k_max, *out)
+    for step in range(steps):
+        d, l, m, p = [t.cpu().numpy() for t in out]
+        od, ol, om, oj = oracle.draft(host, start.n_min, start.n_max, start.k_max)
+        bad = np.nonzero((m != om) | (p != oj) | (l != ol) | np.any(d != od, axis=1))[0]
+        assert bad.size == 0, f"step {step}: request {bad[:1]} differs"
+        counts, fresh = wl.stream_step_draws(step)
+        tok = wl.compose_append(d, l, counts, fresh)
+        host = [np.concatenate([h, tok[b, :counts[b]]]) for b, h in enumerate(host)]
+        for t in out:
+            t.fill_(-7)
+        B.pld_append_draft_store(ctx, torch.from_numpy(tok).cuda(), tok.shape[1],
+                                 torch.from_numpy(counts).cuda(), nb, start.n_min, start.n_max,
+                                 start.k_max, *out)
+    assert B.pld_sync(ctx) == B.PLD_OK
+
+
+@pytest.mark.parametrize("mode", ["indexed", "indexed_collisions", "scan"])
+def test_append_draft_streaming(mode):
+    start = wl.config5_start()
+    if mode == "scan":
+        ctx = B.pld_create(start.batch, wl.STREAM_MAX_LEN, own_store=True)
+    else:
+        ctx = B.pld_create_indexed(start.batch, wl.STREAM_MAX_LEN, start.n_min, start.n_max)
+    try:
+        steps = 300 if mode == "indexed_collisions" else wl.STREAM_STEPS
+        _stream_with_append_draft(ctx, steps, fp_bits=6 if mode == "indexed_collisions" else None)
+    finally:
+        B.pld_destroy(ctx)
+
+
+def test_append_draft_rejected_and_errors():
+    """A rejected append drafts its row as it stands; argument errors are
+    caught before anything is enqueued (the store is unchanged)."""
+    import torch
+    s = IndexedStore(2, 50, 3, 8)
+    try:
+        s.append([np.arange(40, dtype=np.int32) % 6, np.arange(45, dtype=np.int32) % 4])
+        out = B.alloc_outputs(2, 8)
+        tok = torch.tensor([[1, 2, 3, 4, 5, 0, 0, 0], [1, 2, 3, 0, 1, 2, 3, 0]],
+                           dtype=torch.int32, device="cuda")
+        B.pld_append_draft_store(s.ctx, tok, 8, torch.tensor([5, 8], dtype=torch.int32,
+                                                             device="cuda"), 2, 3, 8, 8, *out)
+        assert B.pld_sync(s.ctx) == B.PLD_ECAPACITY   # request 1 would pass max_len
+        s.host[0] = np.concatenate([s.host[0], np.arange(1, 6, dtype=np.int32)])
+        d, l, m, p = [t.cpu().numpy() for t in out]
+        od, ol, om, oj = oracle.draft(s.host, 3, 8, 8)
+        assert np.array_equal(d, od) and np.array_equal(l, ol) and np.array_equal(m, om)
+        assert np.array_equal(p, oj)
+        cnt = torch.tensor([1, 1], dtype=torch.int32, device="cuda")
+        for args in [(2, 9, 8), (3, 2, 8), (3, 8, 0)]:
+            with pytest.raises(B.PldError):
+                B.pld_append_draft_store(s.ctx, tok, 8, cnt, 2, *args, *out)
+        s.check(3, 8, 8, "store unchanged by rejected calls")
+    finally:
+        s.close()
