@@ -360,59 +360,142 @@ __global__ __launch_bounds__(kWave) void pld_index_draft(IndexArgs a, int32_t n_
                        out_draft, out_len, out_match, out_pos, suf);
 }
 
-// pld_append_draft_store on an indexed context, one workgroup per request:
-// the append's inserts, the copy, then (once every insert is performed) the
-// draft of the new history by the first wavefront, which reads new tokens
-// from the source rows, and finally the new length.
-__global__ __launch_bounds__(256) void pld_append_draft_indexed(
+// pld_append_draft_store on an indexed context, one workgroup per request.
+// The draft of the new history needs, per length n, the most recent end of
+// the suffix n-gram among the ends the append adds (old L - 1 .. new L - 2)
+// and among the older ones. The first wavefront finds the newer ones
+// exactly by comparing the suffix with the append's LDS window, and probes
+// the tables for the older ones as soon as the suffix is known, while the
+// other three wavefronts insert the append's n-grams (a probe that meets a
+// slot claimed meanwhile sees a valid table state: slots only fill). Per
+// length the newer end wins when there is one; of the longest length found,
+// an end that came from a table is confirmed against the history (with the
+// draft tokens in the same round trip), and one that does not confirm
+// sends the request to an exact scan. Then the copy and the new length.
+constexpr int kAppendThreads = 256;
+
+__global__ __launch_bounds__(kAppendThreads) void pld_append_draft_indexed(
     IndexArgs a, const int32_t *tokens, int64_t tokens_stride, const int32_t *counts,
     int32_t n_min, int32_t n_max, int32_t k_max, int32_t *out_draft, int32_t *out_len,
     int32_t *out_match, int32_t *out_pos)
 {
-    __shared__ int s_ok;
     __shared__ int32_t win[kAppendWindow];
     __shared__ int32_t suf[kWave];
     const int b = blockIdx.x;
+    const int tid = threadIdx.x;
     const int32_t old_len = a.lengths[b];
     const int32_t c = counts[b];
-    if (threadIdx.x == 0) {
-        const bool ok = append_ok(a, old_len, c);
-        if (!ok)
-            atomicOr(a.err, c < 0 ? kErrAppendNegative : kErrAppendCapacity);
-        s_ok = ok;
-    }
-    __syncthreads();
+    const bool ok = append_ok(a, old_len, c);
+    if (tid == 0 && !ok)
+        atomicOr(a.err, c < 0 ? kErrAppendNegative : kErrAppendCapacity);
     // a rejected append leaves the history as it was; it is still drafted
-    const bool ok = s_ok;
     const int32_t base_len = old_len >= 0 && old_len <= a.max_len ? old_len : 0;
     const int32_t add = ok ? c : 0;
     int32_t *row = a.store + (int64_t)b * a.pitch;
     const int32_t *src = tokens + (int64_t)b * tokens_stride;
-    AppendView v{row, src, base_len};
+    const AppendView v{row, src, base_len};
     const int64_t new_len = (int64_t)base_len + add;
-    if (add > 0) {
-        const int64_t e_first = base_len > 0 ? base_len - 1 : 0;
-        const int64_t q0 = e_first - (a.n_hi - 1) > 0 ? e_first - (a.n_hi - 1) : 0;
-        const int64_t nw = new_len - 1 - q0;
-        if (nw <= kAppendWindow) {
-            for (int64_t i = threadIdx.x; i < nw; i += blockDim.x)
-                win[i] = v.at(q0 + i);
-            __syncthreads();
-            insert_pairs(a, b, v, new_len, threadIdx.x, blockDim.x, LdsTok{win, q0});
-        } else {
-            insert_pairs(a, b, v, new_len, threadIdx.x, blockDim.x, MemTok{&v});
+    const int32_t L = (int32_t)new_len;
+    const int64_t e_first = base_len > 0 ? base_len - 1 : 0;  // first new end
+    const int64_t q0 = e_first - (a.n_hi - 1) > 0 ? e_first - (a.n_hi - 1) : 0;
+    const int64_t nw = new_len - 1 - q0;                       // window tokens
+    const bool in_lds = add > 0 && nw <= kAppendWindow;
+
+    // first wavefront: suffix, hashes and table probes
+    const int lane = tid & (kWave - 1);
+    const int32_t mhat = L - 1 < n_max ? L - 1 : n_max;
+    const int n = lane + 1;
+    const bool active = n >= n_min && n <= mhat;
+    int32_t tok = 0;
+    u64 f = 0;
+    int64_t q_tab = -1;
+    if (tid < kWave) {
+        tok = lane < mhat ? v.at(L - 1 - lane) : 0;
+        u64 h = kHashSeed, mine = 0;
+        for (int i = 0; i < mhat; ++i) {
+            h = hstep(h, __builtin_amdgcn_readlane(tok, i));
+            if (lane == i)
+                mine = h;
         }
-        for (int32_t t = threadIdx.x; t < add; t += blockDim.x)
-            row[base_len + t] = src[t];
+        f = hfinal(mine);
+        if (active)
+            q_tab = probe_fp<true>(table_of(a, b, n), a.cap, a.fp_mask, f);
+        suf[lane] = tok;
     }
-    // every insert (and copy) performed before the first wavefront probes
-    __builtin_amdgcn_s_waitcnt(0);
+    // every thread stages the window
+    if (in_lds)
+        for (int64_t i = tid; i < nw; i += kAppendThreads)
+            win[i] = v.at(q0 + i);
     __syncthreads();
-    if (threadIdx.x < kWave)
-        index_query<true>(a, b, threadIdx.x, (int32_t)new_len, MemTok{&v}, n_min, n_max, k_max,
-                          out_draft, out_len, out_match, out_pos, suf);
-    if (threadIdx.x == 0 && add > 0)
-        a.lengths[b] = (int32_t)new_len;
+    if (tid >= kWave) {
+        // the other wavefronts insert the append's n-grams
+        if (add > 0) {
+            if (in_lds)
+                insert_pairs(a, b, v, new_len, tid - kWave, kAppendThreads - kWave,
+                             LdsTok{win, q0});
+            else
+                insert_pairs(a, b, v, new_len, tid - kWave, kAppendThreads - kWave, MemTok{&v});
+        }
+        for (int32_t t = tid - kWave; t < add; t += kAppendThreads - kWave)
+            row[base_len + t] = src[t];
+        return;
+    }
+
+    // the newest end among the append's ends whose n tokens are the suffix
+    // n-gram (exact, from the window or the view)
+    int64_t q_new = -1;
+    if (active && add > 0) {
+        for (int64_t e = new_len - 2; e >= e_first && q_new < 0; --e) {
+            if (e - n + 1 < 0)
+                break;
+            bool same = true;
+            for (int i = 0; same && i < n; ++i)
+                same = (in_lds ? win[e - i - q0] : v.at(e - i)) == suf[i];
+            if (same)
+                q_new = e;
+        }
+    }
+    const bool from_table = q_new < 0;
+    const int64_t q = from_table ? q_tab : q_new;
+    u64 key = wave_max(active && q >= 0 ? ((u64)(uint32_t)n << 32) | (uint32_t)q : 0);
+    int32_t m = 0, d = 0, e = -1;
+    if (key != 0) {
+        m = (int32_t)(key >> 32);
+        e = (int32_t)(key & 0xffffffffu);
+        const int32_t follow = L - 1 - e;
+        d = follow < k_max ? follow : k_max;
+    }
+    // an end from a table is confirmed with the draft tokens' round trip
+    const bool check = key != 0 && __builtin_amdgcn_readlane((int)from_table, m - 1) != 0;
+    const bool in_range = key != 0 && e <= L - 2 && e - m + 1 >= 0;
+    const bool agree = !(check && in_range && lane < m) || v.at(e - lane) == tok;
+    int32_t cont = in_range && lane < d ? v.at((int64_t)e + 1 + lane) : -1;
+    if (check && !(in_range && __all(agree))) {
+        // two n-grams share a fingerprint: answer by scanning the history
+        key = scan_row(MemTok{&v}, L, mhat, n_min, suf, lane);
+        m = 0, d = 0, e = -1;
+        if (key != 0) {
+            m = (int32_t)(key >> 32);
+            e = (int32_t)(key & 0xffffffffu);
+            const int32_t follow = L - 1 - e;
+            d = follow < k_max ? follow : k_max;
+        }
+        cont = lane < d ? v.at((int64_t)e + 1 + lane) : -1;
+    }
+    int32_t *orow = out_draft + (int64_t)b * k_max;
+    if (lane < k_max)
+        orow[lane] = cont;
+    for (int t = lane + kWave; t < k_max; t += kWave)
+        orow[t] = t < d ? v.at((int64_t)e + 1 + t) : -1;
+    if (lane == 0) {
+        out_len[b] = d;
+        out_match[b] = m;
+        if (out_pos)
+            out_pos[b] = key != 0 ? e - m + 1 : -1;
+        // every thread read the old length before the barrier
+        if (add > 0)
+            a.lengths[b] = L;
+    }
 }
 
 __global__ __launch_bounds__(256) void pld_fill_u64(u64 *p, int64_t n)
