@@ -7,9 +7,10 @@ CPU-baseline leg of ``bench.py`` may import this package. The product library
 The arithmetic lives in ``pld_oracle.c`` (lookup drafting: HyperQwen
 lookup-drafting page, step 1 of the three-step principle) and
 ``fuse_oracle.c`` (draft fusion and long-block scheduling: steps 2 and 3 of
-the same page), plain single-threaded C compiled with gcc at -O2 without
-vector intrinsics; this wrapper only marshals numpy arrays. The rules are
-stated at the top of each file.
+the same page) and ``control_oracle.c`` (the online cost/benefit controller:
+Strata prompt-lookup page, section 5), plain single-threaded C compiled with
+gcc at -O2 without vector intrinsics; this wrapper only marshals numpy
+arrays. The rules are stated at the top of each file.
 """
 
 from __future__ import annotations
@@ -21,7 +22,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "pld_oracle.c"), os.path.join(_HERE, "fuse_oracle.c")]
+_SRCS = [os.path.join(_HERE, "pld_oracle.c"), os.path.join(_HERE, "fuse_oracle.c"),
+         os.path.join(_HERE, "control_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "libpld_oracle.so")
 _lib = None
 
@@ -29,8 +31,11 @@ _lib = None
 def compile_lib(out_path: str, sources=None) -> str:
     """Compile the oracle sources (default: this package's) into a shared
     library at out_path with gcc."""
-    subprocess.run(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror",
-                    "-fPIC", "-shared", "-o", out_path, *(sources or _SRCS)], check=True)
+    # -ffp-contract=off: the controller's double arithmetic rounds each
+    # operation on its own, as its file states
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-Wall", "-Wextra",
+                    "-Werror", "-fPIC", "-shared", "-o", out_path, *(sources or _SRCS)],
+                   check=True)
     return out_path
 
 
@@ -72,6 +77,11 @@ def _bind(lib):
     lib.fuse_oracle_batch.argtypes = [ctypes.POINTER(FuseParams), ctypes.c_int32, i32p,
                                       ctypes.c_int32, i32p, i32p, i32p, i32p, i32p, i32p,
                                       i32p, u64p]
+    lib.control_oracle_batch.restype = ctypes.c_int
+    lib.control_oracle_batch.argtypes = [ctypes.POINTER(ControlParams), ctypes.c_int32, i32p,
+                                         ctypes.POINTER(ctypes.c_double), i32p, i32p,
+                                         ctypes.POINTER(ctypes.c_double), i32p,
+                                         ctypes.POINTER(ctypes.c_double)]
     return lib
 
 
@@ -99,6 +109,27 @@ class FuseParams(ctypes.Structure):
 #: words of per-request fusion state (long flag, hold, near-full run, previous
 #: block positions); all zero before a request's first step
 FUSE_STATE_WORDS = 4
+
+
+class ControlParams(ctypes.Structure):
+    """Controller parameters (Strata prompt-lookup page, section 5): lookup
+    must beat the MTP draft by 5% (margin 1.05); the MTP layer drafts 3
+    tokens (section 1). alpha, beta, the priors and the bucket edges are
+    readings (the page gives no numbers)."""
+    _fields_ = [("alpha", ctypes.c_double), ("beta", ctypes.c_double),
+                ("margin", ctypes.c_double), ("prior_accept", ctypes.c_double),
+                ("prior_time", ctypes.c_double), ("mtp_tokens", ctypes.c_int32),
+                ("edge", ctypes.c_int32 * 3)]
+
+    def __init__(self, alpha=0.1, beta=0.1, margin=1.05, prior_accept=0.5, prior_time=1.0,
+                 mtp_tokens=3, edge=(6, 8, 12)):
+        super().__init__(alpha, beta, margin, prior_accept, prior_time, mtp_tokens,
+                         (ctypes.c_int32 * 3)(*edge))
+
+
+#: doubles of per-request controller state; all zero before the first step
+CONTROL_STATE_WORDS = 11
+SRC_PLAIN, SRC_MTP, SRC_LOOKUP = 0, 1, 2
 
 
 def draft(histories, n_min: int, n_max: int, k_max: int, lib=None):
@@ -166,3 +197,30 @@ def fuse(params: FuseParams, lookup, lookup_len, lookup_match, drafter, accepted
     if rc != 0:
         raise OracleError(f"fusion oracle rejected arguments (rc={rc})")
     return block, positions, src, st
+
+
+def control(params: ControlParams, accepted, round_time, lookup_len, lookup_match, state,
+            lib=None):
+    """One controller step for a batch (Strata prompt-lookup page, section
+    5). accepted [B] int32 and round_time [B] float64: the previous round's
+    outcome (ignored at a request's first step); lookup_len, lookup_match
+    [B] int32: this round's lookup draft; state [B, 11] float64. Returns
+    (source [B] int32, rates [B, 3] float64, new state); inputs unchanged."""
+    lib = load() if lib is None else lib
+    acc = np.ascontiguousarray(accepted, dtype=np.int32)
+    batch = acc.size
+    rt = np.ascontiguousarray(round_time, dtype=np.float64)
+    ll = np.ascontiguousarray(lookup_len, dtype=np.int32)
+    lm = np.ascontiguousarray(lookup_match, dtype=np.int32)
+    st = np.array(state, dtype=np.float64).reshape(batch, CONTROL_STATE_WORDS).copy()
+    src = np.empty(batch, np.int32)
+    rates = np.empty((batch, 3), np.float64)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    rc = lib.control_oracle_batch(ctypes.byref(params), batch, acc.ctypes.data_as(i32p),
+                                  rt.ctypes.data_as(f64p), ll.ctypes.data_as(i32p),
+                                  lm.ctypes.data_as(i32p), st.ctypes.data_as(f64p),
+                                  src.ctypes.data_as(i32p), rates.ctypes.data_as(f64p))
+    if rc != 0:
+        raise OracleError(f"controller oracle rejected arguments (rc={rc})")
+    return src, rates, st

@@ -83,9 +83,10 @@ def test_mutant_is_caught(name, tmp_path):
     c = tmp_path / f"{name}.c"
     so = tmp_path / f"{name}.so"
     c.write_text(mutated)
-    fuse_src = os.path.join(os.path.dirname(SRC), "fuse_oracle.c")
-    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", str(so),
-                    str(c), fuse_src], check=True)
+    here = os.path.dirname(SRC)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-o",
+                    str(so), str(c), os.path.join(here, "fuse_oracle.c"),
+                    os.path.join(here, "control_oracle.c")], check=True)
     lib = oracle.load(str(so))
     assert _pins_fail(lib), f"mutant {name} passed every pin"
 
