@@ -347,12 +347,73 @@ pld_status pld_draft_fuse_batch(pld_ctx *ctx, const int32_t *const *histories,
                                 int32_t *out_positions, uint64_t *out_src, hipStream_t stream);
 
 /*
+ * Online cost/benefit controller (Strata prompt-lookup page, section 5).
+ *
+ * Per request and step it chooses between the lookup draft, the model's own
+ * draft layer (MTP) and plain decoding, from running estimates of each
+ * one's committed tokens per unit of verify time: the lookup's acceptance
+ * in 4 match-length buckets, MTP's acceptance, and each source's round
+ * time, all exponential moving averages of measured outcomes. The lookup
+ * draft is chosen only when its estimate is at least `margin` times MTP's
+ * (the page: 5% better); otherwise MTP when it beats plain decoding, else
+ * plain decoding. Readings where the page gives no number or formula:
+ * acceptance is accepted / drafted tokens of a round; a round commits its
+ * accepted tokens plus one; the moving averages weigh a new measurement by
+ * alpha (acceptance) and beta (time); estimates start at prior_accept and
+ * prior_time; the buckets start at match lengths 0, bucket_edge[0..2]; ties
+ * go to the draft. Arithmetic is IEEE double with each operation rounded on
+ * its own, so decisions do not depend on the compiler.
+ */
+typedef struct pld_control_params {
+    double alpha;          /* weight of a new acceptance fraction; 0.1 */
+    double beta;           /* weight of a new round time; 0.1 */
+    double margin;         /* the lookup needs margin x MTP's rate; the page: 1.05 */
+    double prior_accept;   /* first acceptance estimate; 0.5 */
+    double prior_time;     /* first round-time estimate, caller's unit; 1.0 */
+    int32_t mtp_tokens;    /* MTP draft tokens per round; the page: 3 */
+    int32_t bucket_edge[3];/* first match length of buckets 1..3; 6, 8, 12 */
+} pld_control_params;
+
+/* doubles of per-request controller state (zeros before the first step) */
+#define PLD_CONTROL_STATE_WORDS 11
+/* sources */
+#define PLD_SOURCE_PLAIN 0
+#define PLD_SOURCE_MTP 1
+#define PLD_SOURCE_LOOKUP 2
+
+/* The defaults above. Errors: PLD_EINVAL (null). */
+pld_status pld_control_params_default(pld_control_params *params);
+
+/*
+ * One controller step for a batch: fold in each request's previous round,
+ * then choose its source for this round.
+ *  accepted:     device int32[batch]: draft tokens the verifier accepted in
+ *                the previous round (read when the request had one).
+ *  round_time:   device double[batch]: that round's measured time (> 0).
+ *  lookup_len, lookup_match: device int32[batch]: this round's lookup draft
+ *                (pld_draft_batch's out_len and out_match; 0 = none).
+ *  state:        device double[batch * PLD_CONTROL_STATE_WORDS], updated.
+ *  out_source:   device int32[batch]: PLD_SOURCE_*.
+ *  out_rates:    device double[batch * 3] or NULL: the estimates the choice
+ *                used (plain, MTP, lookup; 0 for a missing lookup draft).
+ * An outcome out of range (accepted above the round's draft tokens or
+ * negative, a time not > 0) or a negative lookup input is not folded in
+ * and sets the sticky flag (PLD_EINVAL at pld_sync); the choice is still
+ * made.
+ * Errors: PLD_EINVAL (bad params, sizes, pointers), PLD_EHIP.
+ */
+pld_status pld_control(pld_ctx *ctx, const pld_control_params *params, const int32_t *accepted,
+                       const double *round_time, const int32_t *lookup_len,
+                       const int32_t *lookup_match, double *state, int32_t batch,
+                       int32_t *out_source, double *out_rates, hipStream_t stream);
+
+/*
  * Wait for the stream, then report and clear the sticky device-side flag:
  * PLD_OK when clear; PLD_ECAPACITY when a history exceeded max_len (or its
  * row's stride) or an append overflowed; PLD_EINVAL when a length or count
  * was negative, a length was below a strided call's min_len, a row pointer
- * was null or misaligned, or pld_fuse saw inconsistent per-request inputs
- * (capacity wins when both are set).
+ * was null or misaligned, pld_fuse saw inconsistent per-request inputs, or
+ * pld_control an outcome out of range (capacity wins when both are set).
  * Errors: PLD_EINVAL (null ctx), PLD_EHIP.
  */
 pld_status pld_sync(pld_ctx *ctx, hipStream_t stream);

@@ -32,7 +32,8 @@ EXPORTS = ("pld_create", "pld_create_indexed", "pld_destroy", "pld_configure", "
            "pld_draft_batch_pos", "pld_draft_batch_strided", "pld_index_fingerprint_bits",
            "pld_draft_store", "pld_append_draft_store",
            "pld_fuse_params_default",
-           "pld_fuse", "pld_draft_fuse_batch", "pld_sync", "pld_strerror",
+           "pld_fuse", "pld_draft_fuse_batch", "pld_control_params_default", "pld_control",
+           "pld_sync", "pld_strerror",
            "pld_last_error")
 
 _lib = None
@@ -44,6 +45,19 @@ class PldFuseParams(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "head", "positions_long", "replace_min", "agree_min", "agree_tokens",
         "tail_min", "entry_steps", "sticky", "near_full_slack")]
+
+
+class PldControlParams(ctypes.Structure):
+    """pld_control_params (include/pld.h); pld_control_params_default() gives
+    the defaults (the Strata page's margin 1.05 and 3 MTP tokens)."""
+    _fields_ = [("alpha", ctypes.c_double), ("beta", ctypes.c_double),
+                ("margin", ctypes.c_double), ("prior_accept", ctypes.c_double),
+                ("prior_time", ctypes.c_double), ("mtp_tokens", ctypes.c_int32),
+                ("bucket_edge", ctypes.c_int32 * 3)]
+
+
+PLD_CONTROL_STATE_WORDS = 11
+PLD_SOURCE_PLAIN, PLD_SOURCE_MTP, PLD_SOURCE_LOOKUP = 0, 1, 2
 
 
 class PldError(RuntimeError):
@@ -82,6 +96,9 @@ def load(path: str = LIB_PATH):
                      vp, vp, vp, vp],
         "pld_draft_fuse_batch": [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp,
                                  ctypes.POINTER(PldFuseParams), vp, vp, vp, vp, vp, vp, vp],
+        "pld_control_params_default": [ctypes.POINTER(PldControlParams)],
+        "pld_control": [vp, ctypes.POINTER(PldControlParams), vp, vp, vp, vp, vp, i32, vp, vp,
+                        vp],
         "pld_sync": [vp, vp],
     }
     for name, args in sig.items():
@@ -302,6 +319,27 @@ def pld_draft_fuse_batch(ctx: int, histories, lengths, batch: int, n_min: int, n
         _dev_ptr(accepted, "accepted", i32), _dev_ptr(state, "state", i32),
         _dev_ptr(out_block, "out_block", i32), _dev_ptr(out_positions, "out_positions", i32),
         _dev_ptr(out_src, "out_src", torch.int64), _stream(stream)))
+
+
+def pld_control_params_default() -> PldControlParams:
+    p = PldControlParams()
+    _check("pld_control_params_default", load().pld_control_params_default(ctypes.byref(p)))
+    return p
+
+
+def pld_control(ctx: int, params: PldControlParams, accepted, round_time, lookup_len,
+                lookup_match, state, batch: int, out_source, out_rates=None,
+                stream=None) -> None:
+    """One controller step (include/pld.h). `round_time`, `state` and
+    `out_rates` are float64 device tensors."""
+    import torch
+    i32, f64 = _i32(), torch.float64
+    _check("pld_control", load().pld_control(
+        ctx, ctypes.byref(params), _dev_ptr(accepted, "accepted", i32),
+        _dev_ptr(round_time, "round_time", f64), _dev_ptr(lookup_len, "lookup_len", i32),
+        _dev_ptr(lookup_match, "lookup_match", i32), _dev_ptr(state, "state", f64), int(batch),
+        _dev_ptr(out_source, "out_source", i32), _dev_ptr(out_rates, "out_rates", f64),
+        _stream(stream)))
 
 
 def pld_sync(ctx: int, stream=None) -> int:

@@ -612,6 +612,69 @@ pld_status pld_draft_fuse_batch(pld_ctx *ctx, const int32_t *const *histories,
                  out_len, out_match, nullptr, stream, &f);
 }
 
+pld_status pld_control_params_default(pld_control_params *params)
+{
+    if (!params)
+        return fail(PLD_EINVAL, "params is null");
+    // Strata prompt-lookup page, section 5: the lookup must beat the MTP
+    // draft by 5%; section 1: the MTP layer drafts 3 tokens. The weights,
+    // priors and bucket edges are readings.
+    *params = pld_control_params{0.1, 0.1, 1.05, 0.5, 1.0, 3, {6, 8, 12}};
+    return PLD_OK;
+}
+
+pld_status pld_control(pld_ctx *ctx, const pld_control_params *params, const int32_t *accepted,
+                       const double *round_time, const int32_t *lookup_len,
+                       const int32_t *lookup_match, double *state, int32_t batch,
+                       int32_t *out_source, double *out_rates, hipStream_t stream)
+{
+    if (!ctx)
+        return fail(PLD_EINVAL, "ctx is null");
+    if (!params)
+        return fail(PLD_EINVAL, "params is null");
+    const pld_control_params &p = *params;
+    if (!(p.alpha >= 0.0 && p.alpha <= 1.0 && p.beta >= 0.0 && p.beta <= 1.0))
+        return fail(PLD_EINVAL, "alpha and beta must be in [0, 1]");
+    if (!(p.margin > 0.0) || !(p.prior_accept >= 0.0 && p.prior_accept <= 1.0) ||
+        !(p.prior_time > 0.0))
+        return fail(PLD_EINVAL, "need margin > 0, prior_accept in [0, 1], prior_time > 0");
+    if (p.mtp_tokens < 0 || p.bucket_edge[0] > p.bucket_edge[1] ||
+        p.bucket_edge[1] > p.bucket_edge[2])
+        return fail(PLD_EINVAL, "need mtp_tokens >= 0 and nondecreasing bucket edges");
+    if (batch < 0 || batch > ctx->max_batch)
+        return fail(PLD_EINVAL, "batch %d outside [0, max_batch=%d]", batch, ctx->max_batch);
+    if (batch == 0)
+        return PLD_OK;
+    if (!accepted || !round_time || !lookup_len || !lookup_match || !state || !out_source)
+        return fail(PLD_EINVAL, "null buffer pointer");
+    if ((((uintptr_t)accepted | (uintptr_t)lookup_len | (uintptr_t)lookup_match |
+          (uintptr_t)out_source) & 3u) ||
+        (((uintptr_t)round_time | (uintptr_t)state | (uintptr_t)out_rates) & 7u))
+        return fail(PLD_EINVAL, "misaligned buffer (int32: 4 bytes, double: 8 bytes)");
+    pld::ControlArgs a;
+    a.alpha = p.alpha;
+    a.beta = p.beta;
+    a.margin = p.margin;
+    a.prior_accept = p.prior_accept;
+    a.prior_time = p.prior_time;
+    a.mtp_tokens = p.mtp_tokens;
+    for (int i = 0; i < 3; ++i)
+        a.edge[i] = p.bucket_edge[i];
+    a.accepted = accepted;
+    a.round_time = round_time;
+    a.lookup_len = lookup_len;
+    a.lookup_match = lookup_match;
+    a.state = state;
+    a.batch = batch;
+    a.out_source = out_source;
+    a.out_rates = out_rates;
+    a.err = ctx->err;
+    hipError_t e = pld::launch_control(a, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "control kernel launch");
+    return PLD_OK;
+}
+
 pld_status pld_sync(pld_ctx *ctx, hipStream_t stream)
 {
     if (!ctx)
@@ -631,12 +694,13 @@ pld_status pld_sync(pld_ctx *ctx, hipStream_t stream)
                     (bits & pld::kErrLenCapacity) ? "a history longer than max_len " : "",
                     (bits & pld::kErrAppendCapacity) ? "an append past max_len" : "");
     if (bits)
-        return fail(PLD_EINVAL, "device reported: %s%s%s%s%s",
+        return fail(PLD_EINVAL, "device reported: %s%s%s%s%s%s",
                     (bits & pld::kErrLenNegative) ? "a negative length " : "",
                     (bits & pld::kErrBadRow) ? "a null or misaligned row pointer " : "",
                     (bits & pld::kErrAppendNegative) ? "a negative append count " : "",
                     (bits & pld::kErrBelowMinLen) ? "a length below the promised min_len " : "",
-                    (bits & pld::kErrFuseInput) ? "inconsistent fusion inputs" : "");
+                    (bits & pld::kErrFuseInput) ? "inconsistent fusion inputs " : "",
+                    (bits & pld::kErrControlInput) ? "a controller outcome out of range" : "");
     return PLD_OK;
 }
 

@@ -20,7 +20,8 @@ enum : uint32_t {
     kErrAppendCapacity = 8u,  // append would pass max_len
     kErrAppendNegative = 16u, // counts[b] < 0
     kErrBelowMinLen = 32u,    // strided batch: lengths[b] < the caller's min_len
-    kErrFuseInput = 64u       // pld_fuse: inconsistent per-request inputs
+    kErrFuseInput = 64u,      // pld_fuse: inconsistent per-request inputs
+    kErrControlInput = 128u   // pld_control: an outcome or lookup input out of range
 };
 
 // Per-request reduction state: the packed key maximum and the arrival
@@ -97,6 +98,22 @@ struct IndexArgs {
     unsigned int *err;
 };
 
+// The online cost/benefit controller (pld_control.hip).
+struct ControlArgs {
+    double alpha, beta, margin, prior_accept, prior_time;
+    int32_t mtp_tokens;
+    int32_t edge[3];
+    const int32_t *accepted;      // [batch]
+    const double *round_time;     // [batch]
+    const int32_t *lookup_len;    // [batch]
+    const int32_t *lookup_match;  // [batch]
+    double *state;                // [batch * 11]
+    int32_t batch;
+    int32_t *out_source;          // [batch]
+    double *out_rates;            // [batch * 3] or null
+    unsigned int *err;
+};
+
 // Workgroups the scan launches for a batch (tiles per request x batch).
 int64_t scan_grid(int32_t max_len, int32_t batch, int tile_tokens);
 
@@ -119,6 +136,7 @@ hipError_t launch_index_draft(const IndexArgs &a, int32_t batch, int32_t n_min, 
                               int32_t k_max, int32_t *out_draft, int32_t *out_len,
                               int32_t *out_match, int32_t *out_pos, hipStream_t s);
 hipError_t launch_index_clear(const IndexArgs &a, int32_t batch, hipStream_t s);
+hipError_t launch_control(const ControlArgs &a, hipStream_t s);
 
 }  // namespace pld
 

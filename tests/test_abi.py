@@ -104,3 +104,12 @@ def test_create_indexed_rejects_bad_lengths_before_any_hip_call():
         assert "n_min" in B.pld_last_error()
     assert _raw("pld_draft_store", None, 1, 4, 12, 16, None, None, None, None,
                 None) == B.PLD_EINVAL
+
+
+def test_control_params_default():
+    """Strata prompt-lookup page, sections 1 and 5: MTP drafts 3 tokens, the
+    lookup must be 5% better; the rest are the readings stated in pld.h."""
+    p = B.pld_control_params_default()
+    assert (p.alpha, p.beta, p.margin, p.prior_accept, p.prior_time, p.mtp_tokens) == \
+        (0.1, 0.1, 1.05, 0.5, 1.0, 3)
+    assert list(p.bucket_edge) == [6, 8, 12]
