@@ -96,6 +96,9 @@ def parse():
     ap.add_argument("--stream-start", type=int, default=0,
                     help="workload 5 only: start histories of this many tokens instead "
                          "of 32,768 (the same decode on longer histories)")
+    ap.add_argument("--control", action="store_true",
+                    help="workload 5 only: each step also runs the online cost/benefit "
+                         "controller (pld_control) on the step's lookup drafts")
     ap.add_argument("--append-draft", action="store_true",
                     help="workload 5 only: each step's append and the next step's draft "
                          "as one pld_append_draft_store call")
@@ -489,6 +492,17 @@ def bench_stream(args, torch, B, wl, dev):
     else:
         ctx = B.pld_create(nb, max_len, own_store=True)
     rows, lens = B.pld_store_views(ctx)
+    # controller inputs: every outcome "0 accepted in time 1.0" is valid for
+    # any previous choice, so the captured steps need no host round trip
+    cparams = B.pld_control_params_default()
+    c_state = torch.zeros((nb, B.PLD_CONTROL_STATE_WORDS), dtype=torch.float64, device=dev)
+    c_acc = torch.zeros(nb, dtype=torch.int32, device=dev)
+    c_time = torch.ones(nb, dtype=torch.float64, device=dev)
+    c_src = torch.empty(nb, dtype=torch.int32, device=dev)
+
+    def control():
+        if args.control:
+            B.pld_control(ctx, cparams, c_acc, c_time, out[1], out[2], c_state, nb, c_src)
 
     def draft():
         if args.index:
@@ -538,14 +552,17 @@ def bench_stream(args, torch, B, wl, dev):
         if args.append_draft:
             # draft(0), then append(s) + draft(s + 1) per call, then the last append
             draft()
+            control()
             for step in range(steps_n - 1):
                 B.pld_append_draft_store(ctx, toks_d[step], width, cnts_d[step], nb,
                                          start.n_min, start.n_max, start.k_max, out[0], out[1],
                                          out[2])
+                control()
             B.pld_append(ctx, toks_d[steps_n - 1], width, cnts_d[steps_n - 1], nb)
         else:
             for step in range(steps_n):
                 draft()
+                control()
                 B.pld_append(ctx, toks_d[step], width, cnts_d[step], nb)
     times = []
     reps = max(1, args.steps // steps_n) if args.steps >= steps_n else 1
@@ -586,7 +603,8 @@ def bench_stream(args, torch, B, wl, dev):
                    "steps": steps_n, "n_min": start.n_min, "n_max": start.n_max,
                    "k_max": start.k_max, "mean_bytes_per_step": round(bytes_mean),
                    "drafting": "n-gram index" if args.index else "scan",
-                   "calls_per_step": 1 if args.append_draft else 2},
+                   "calls_per_step": (1 if args.append_draft else 2) + int(args.control),
+                   "controller": bool(args.control)},
         "us_per_step_append_plus_draft": round(gpu_s * 1e6 / steps_n, 3),
         # for the index: the history bytes a scan would have read, per second
         ("scan_equivalent_GBps" if args.index else "scan_GBps"):
