@@ -102,6 +102,9 @@ def parse():
     ap.add_argument("--append-draft", action="store_true",
                     help="workload 5 only: each step's append and the next step's draft "
                          "as one pld_append_draft_store call")
+    ap.add_argument("--library-read", action="store_true",
+                    help="also time torch.amax over the same rotated copies (a library "
+                         "full read of the same bytes, for context)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with 8 plain 64 MiB device copies (a counter "
                          "reference of known size for rocprofv3 --pmc)")
@@ -248,6 +251,29 @@ def main():
         warm = {"us_per_step": warm_us, "GBps": bytes_step / warm_us / 1e3,
                 "note": "same copy every step (Infinity-Cache resident)"}
 
+    library = None
+    if args.library_read:
+        # torch's own full reduction over each rotated copy, graph-replayed
+        flat = [b.reshape(-1) for b in (bufs if args.layout == "strided" else
+                                         [c.flat for c in copies])]
+        red = torch.empty((), dtype=torch.int32, device=dev)
+        g3 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g3, stream=cap_stream):
+            for i in range(G):
+                torch.amax(flat[i % rot], 0, out=red)
+        torch.cuda.synchronize()
+        g3.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g3.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        lib_us = e0.elapsed_time(e1) * 1e3 / steps
+        library = {"op": "torch.amax over the same rotated copies", "us_per_launch": lib_us,
+                   "GBps": flat[0].numel() * 4 / lib_us / 1e3}
+
     assert B.pld_sync(ctx) == B.PLD_OK
     got = [t.cpu().numpy() for t in out[:3]]
     B.pld_destroy(ctx)
@@ -298,6 +324,8 @@ def main():
     }
     if warm:
         rec["warm"] = warm
+    if library:
+        rec["library_full_read"] = library
 
     if not args.no_cpu_baseline:
         import oracle
