@@ -7,8 +7,9 @@ CPU-baseline leg of ``bench.py`` may import this package. The product library
 The arithmetic lives in ``pld_oracle.c`` (lookup drafting: HyperQwen
 lookup-drafting page, step 1 of the three-step principle) and
 ``fuse_oracle.c`` (draft fusion and long-block scheduling: steps 2 and 3 of
-the same page) and ``control_oracle.c`` (the online cost/benefit controller:
-Strata prompt-lookup page, section 5), plain single-threaded C compiled with
+the same page), ``control_oracle.c`` (the online cost/benefit controller:
+Strata prompt-lookup page, section 5) and ``ngram_oracle.c`` (successor-count
+n-gram drafting: llama.cpp page, its context cache), plain single-threaded C compiled with
 gcc at -O2 without vector intrinsics; this wrapper only marshals numpy
 arrays. The rules are stated at the top of each file.
 """
@@ -23,20 +24,27 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRCS = [os.path.join(_HERE, "pld_oracle.c"), os.path.join(_HERE, "fuse_oracle.c"),
-         os.path.join(_HERE, "control_oracle.c")]
+         os.path.join(_HERE, "control_oracle.c"), os.path.join(_HERE, "ngram_oracle.c")]
 _LIB_PATH = os.path.join(_HERE, "libpld_oracle.so")
 _lib = None
 
 
-def compile_lib(out_path: str, sources=None) -> str:
+def compile_lib(out_path: str, sources=None, strict: bool = True) -> str:
     """Compile the oracle sources (default: this package's) into a shared
-    library at out_path with gcc."""
+    library at out_path with gcc; strict turns warnings into errors."""
     # -ffp-contract=off: the controller's double arithmetic rounds each
     # operation on its own, as its file states
-    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-Wall", "-Wextra",
-                    "-Werror", "-fPIC", "-shared", "-o", out_path, *(sources or _SRCS)],
-                   check=True)
+    warn = ["-Wall", "-Wextra", "-Werror"] if strict else []
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", *warn, "-fPIC", "-shared",
+                    "-o", out_path, *(sources or _SRCS)], check=True)
     return out_path
+
+
+def sources(replace=None) -> list:
+    """This package's C sources, with {file name: other path} swapped in (a
+    test's planted-mistake copy of one file)."""
+    replace = replace or {}
+    return [replace.get(os.path.basename(s), s) for s in _SRCS]
 
 
 def build(force: bool = True) -> str:
@@ -82,6 +90,10 @@ def _bind(lib):
                                          ctypes.POINTER(ctypes.c_double), i32p, i32p,
                                          ctypes.POINTER(ctypes.c_double), i32p,
                                          ctypes.POINTER(ctypes.c_double)]
+    lib.ngram_oracle_draft_batch.restype = ctypes.c_int
+    lib.ngram_oracle_draft_batch.argtypes = [ctypes.POINTER(NgramParams),
+                                             ctypes.POINTER(i32p), i64p, ctypes.c_int32,
+                                             ctypes.c_int32, i32p, i32p, i32p]
     return lib
 
 
@@ -130,6 +142,25 @@ class ControlParams(ctypes.Structure):
 #: doubles of per-request controller state; all zero before the first step
 CONTROL_STATE_WORDS = 11
 SRC_PLAIN, SRC_MTP, SRC_LOOKUP = 0, 1, 2
+
+#: longest context of the successor-count drafter (llama.cpp page: sizes 1 to 4)
+NGRAM_MAX_N = 4
+
+
+class NgramParams(ctypes.Structure):
+    """Successor-count drafting parameters (llama.cpp page, its context
+    cache): contexts of 1 to 4 tokens, longest tried first; per length n
+    (index n - 1) the context must have been followed at least min_count
+    times and its most frequent successor must hold at least min_percent of
+    those. The page gives 1 and 50 for the 4-gram; every length uses them by
+    default (a reading)."""
+    _fields_ = [("n_min", ctypes.c_int32), ("n_max", ctypes.c_int32),
+                ("min_count", ctypes.c_int32 * NGRAM_MAX_N),
+                ("min_percent", ctypes.c_int32 * NGRAM_MAX_N)]
+
+    def __init__(self, n_min=1, n_max=4, min_count=(1, 1, 1, 1), min_percent=(50, 50, 50, 50)):
+        super().__init__(n_min, n_max, (ctypes.c_int32 * NGRAM_MAX_N)(*min_count),
+                         (ctypes.c_int32 * NGRAM_MAX_N)(*min_percent))
 
 
 def draft(histories, n_min: int, n_max: int, k_max: int, lib=None):
@@ -224,3 +255,28 @@ def control(params: ControlParams, accepted, round_time, lookup_len, lookup_matc
     if rc != 0:
         raise OracleError(f"controller oracle rejected arguments (rc={rc})")
     return src, rates, st
+
+
+def ngram_draft(params: NgramParams, histories, k_max: int, lib=None):
+    """Successor-count drafts for a batch (llama.cpp page, its context
+    cache). histories: sequence of 1-D int32 arrays. Returns (draft [B, k_max]
+    int32 padded with -1, draft_len [B] int32, levels [B, k_max] int32: the
+    context length behind each draft token, 0 past draft_len)."""
+    lib = load() if lib is None else lib
+    hs = [np.ascontiguousarray(h, dtype=np.int32) for h in histories]
+    batch = len(hs)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    ptrs = (i32p * max(batch, 1))()
+    for b, h in enumerate(hs):
+        ptrs[b] = h.ctypes.data_as(i32p)
+    lengths = np.array([h.size for h in hs], dtype=np.int64)
+    out_draft = np.empty((batch, k_max), dtype=np.int32)
+    out_len = np.empty(batch, dtype=np.int32)
+    levels = np.empty((batch, k_max), dtype=np.int32)
+    rc = lib.ngram_oracle_draft_batch(ctypes.byref(params), ptrs,
+                                      lengths.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                      batch, k_max, out_draft.ctypes.data_as(i32p),
+                                      out_len.ctypes.data_as(i32p), levels.ctypes.data_as(i32p))
+    if rc != 0:
+        raise OracleError(f"n-gram oracle rejected arguments (rc={rc})")
+    return out_draft, out_len, levels
