@@ -38,6 +38,8 @@ if ROOT not in sys.path:
 
 METRIC = ("batched draft steps/s + scanned history GB/s (% HBM peak); "
           "p50 µs per draft step")
+METRIC_NGRAM = ("successor-count n-gram draft steps/s (llama.cpp context cache rule, "
+                "batched, exact)")
 METRIC_FUSE = ("lookup draft + draft fusion and long-block scheduling steps/s "
                "(HyperQwen lookup-drafting page, steps 1-3)")
 PROFILE = os.path.join(ROOT, "profiles", "pld_scan_c4_b16x262144.md")
@@ -90,6 +92,9 @@ def parse():
                          "proposal and schedules the block (one launch: "
                          "pld_draft_fuse_batch; two: pld_draft_batch + pld_fuse); "
                          "row-table layout, workloads 1-4")
+    ap.add_argument("--ngram", action="store_true",
+                    help="draft from the successor-count cache (pld_create_ngram, "
+                         "pld_draft_ngram) instead of the lookup scan")
     ap.add_argument("--index", action="store_true",
                     help="workload 5 only: draft from the context's incremental n-gram "
                          "index (pld_create_indexed, pld_draft_store) instead of scanning")
@@ -141,10 +146,16 @@ def main():
     dev = torch.device("cuda:0")
     B.load()
 
+    if args.ngram and (args.index or args.append_draft or args.fuse != "none"):
+        print("--ngram drafts from the successor-count cache: it does not combine with "
+              "--index, --append-draft or --fuse", file=sys.stderr)
+        sys.exit(2)
     if args.config == 5:
         return bench_stream(args, torch, B, wl, dev)
 
     w = wl.ALL_CONFIGS[args.config]()
+    if args.ngram:
+        return bench_ngram(args, torch, B, wl, dev, w)
     if args.fuse != "none":
         return bench_fuse(args, torch, B, wl, dev, w)
     bytes_step = 4 * w.total_tokens
@@ -504,6 +515,114 @@ def bench_fuse(args, torch, B, wl, dev, w):
     print(json.dumps(rec), flush=True)
 
 
+def bench_ngram(args, torch, B, wl, dev, w):
+    """Successor-count drafting on a lookup workload's histories.
+
+    The cache is built once by appending every history whole (timed on its
+    own: the insert rate), then G draft calls over the batch are captured in
+    a HIP graph and replayed. Each call drafts from the same cache state, so
+    the slots it reads are warm in the caches after the first replay (the
+    streaming leg, --config 5 --ngram, appends between drafts)."""
+    G = max(1, min(args.graph_steps, args.steps))
+    k = w.k_max
+    nb = w.batch
+    max_len = int(w.lengths.max())
+    ctx = B.pld_create_ngram(nb, max_len)
+    params = B.pld_ngram_params_default()
+    width = max_len
+    tok = np.zeros((nb, width), np.int32)
+    for b, h in enumerate(w.histories):
+        tok[b, :len(h)] = h
+    tok_d = torch.from_numpy(tok).to(dev)
+    cnt_d = torch.from_numpy(w.lengths.astype(np.int32)).to(dev)
+    out_d = torch.empty((nb, k), dtype=torch.int32, device=dev)
+    out_l = torch.empty(nb, dtype=torch.int32, device=dev)
+    out_v = torch.empty((nb, k), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    B.pld_append(ctx, tok_d, width, cnt_d, nb)
+    e1.record()
+    torch.cuda.synchronize()
+    build_s = e0.elapsed_time(e1) * 1e-3
+    B.pld_draft_ngram(ctx, params, nb, k, out_d, out_l, out_v)
+    assert B.pld_sync(ctx) == B.PLD_OK
+    ref = (out_d.cpu().numpy(), out_l.cpu().numpy(), out_v.cpu().numpy())
+
+    cap_stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=cap_stream):
+        for _ in range(G):
+            B.pld_draft_ngram(ctx, params, nb, k, out_d, out_l, out_v)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert np.array_equal(out_d.cpu().numpy(), ref[0]), "graph replay differs"
+    reps_w = max(1, args.warmup // G)
+    reps = max(1, -(-args.steps // G))
+    steps = reps * G
+    for _ in range(reps_w):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    gpu_us = e0.elapsed_time(e1) * 1e3 / steps
+    assert B.pld_sync(ctx) == B.PLD_OK
+    B.pld_destroy(ctx)
+    # one dependent lookup round per draft token, plus the one that ends a
+    # draft short of k_max
+    rounds = int(np.max(np.minimum(ref[1] + 1, k)))
+    rec = {
+        "metric": METRIC_NGRAM,
+        "value": round(steps / wall_s, 1),
+        "unit": "draft steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": reps_w * G,
+        "ms_per_step": round(wall_s * 1e3 / steps, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": nb, "history_tokens": max_len,
+                   "n_min": params.n_min, "n_max": params.n_max, "k_max": k,
+                   "min_count": list(params.min_count),
+                   "min_percent": list(params.min_percent), "graph_steps": G},
+        "graph_us_per_step": round(gpu_us, 3),
+        "mean_draft_tokens": round(float(ref[1].mean()), 3),
+        "latency": {"rounds_per_step": rounds, "us_per_round": round(gpu_us / rounds, 3)},
+        "build": {"tokens": int(w.total_tokens), "ms": round(build_s * 1e3, 3),
+                  "tokens_per_s": round(w.total_tokens / build_s, 1)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        op = oracle.NgramParams()
+        n, t_start = 0, time.perf_counter()
+        parity = True
+        while n < G and time.perf_counter() - t_start < args.cpu_seconds:
+            od, ol, ov = oracle.ngram_draft(op, w.histories, k)
+            parity &= (np.array_equal(od, ref[0]) and np.array_equal(ol, ref[1])
+                       and np.array_equal(ov, ref[2]))
+            n += 1
+        el = time.perf_counter() - t_start
+        rec["cpu_baseline"] = {
+            "value": round(n / el, 3), "unit": "draft steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} repeats of the batch's drafts (brute-force recount, {el:.1f} s, "
+                      f"one thread, {cpu_model()})"}
+        rec["parity"] = "bit-exact" if parity else "MISMATCH"
+        if not parity:
+            print(json.dumps(rec))
+            sys.exit(1)
+    print(json.dumps(rec), flush=True)
+
+
 def bench_stream(args, torch, B, wl, dev):
     """The streaming decode: 64 requests from 32,768 tokens, 1,024 steps of
     pld_draft_batch on the context's own store, then pld_append of the 1..16
@@ -517,6 +636,8 @@ def bench_stream(args, torch, B, wl, dev):
     max_len = start_len + steps_n * width
     if args.index:
         ctx = B.pld_create_indexed(nb, max_len, start.n_min, start.n_max)
+    elif args.ngram:
+        ctx = B.pld_create_ngram(nb, max_len)
     else:
         ctx = B.pld_create(nb, max_len, own_store=True)
     rows, lens = B.pld_store_views(ctx)
@@ -532,8 +653,12 @@ def bench_stream(args, torch, B, wl, dev):
         if args.control:
             B.pld_control(ctx, cparams, c_acc, c_time, out[1], out[2], c_state, nb, c_src)
 
+    nparams = B.pld_ngram_params_default()
+
     def draft():
-        if args.index:
+        if args.ngram:
+            B.pld_draft_ngram(ctx, nparams, nb, start.k_max, out[0], out[1], levels)
+        elif args.index:
             B.pld_draft_store(ctx, nb, start.n_min, start.n_max, start.k_max, out[0], out[1],
                               out[2])
         else:
@@ -542,6 +667,7 @@ def bench_stream(args, torch, B, wl, dev):
     init = torch.from_numpy(np.stack(start.histories)).to(dev)
     init_counts = torch.full((nb,), start_len, dtype=torch.int32, device=dev)
     out = B.alloc_outputs(nb, start.k_max, device=dev)
+    levels = torch.zeros((nb, start.k_max), dtype=torch.int32, device=dev)
 
     def restart():
         B.pld_store_reset(ctx)
@@ -557,7 +683,8 @@ def bench_stream(args, torch, B, wl, dev):
     for step in range(steps_n):
         draft()
         d, l = out[0].cpu().numpy(), out[1].cpu().numpy()
-        first_drafts.append((d.copy(), l.copy(), out[2].cpu().numpy()))
+        first_drafts.append((d.copy(), l.copy(),
+                             (levels if args.ngram else out[2]).cpu().numpy()))
         total_tokens += int(lengths.sum())
         counts, fresh = wl.stream_step_draws(step)
         toks[step] = wl.compose_append(d, l, counts, fresh)
@@ -630,22 +757,33 @@ def bench_stream(args, torch, B, wl, dev):
         "config": {"workload": start.name, "batch": nb, "start_tokens": start_len,
                    "steps": steps_n, "n_min": start.n_min, "n_max": start.n_max,
                    "k_max": start.k_max, "mean_bytes_per_step": round(bytes_mean),
-                   "drafting": "n-gram index" if args.index else "scan",
+                   "drafting": ("successor-count cache" if args.ngram else
+                                "n-gram index" if args.index else "scan"),
                    "calls_per_step": (1 if args.append_draft else 2) + int(args.control),
                    "controller": bool(args.control)},
         "us_per_step_append_plus_draft": round(gpu_s * 1e6 / steps_n, 3),
         # for the index: the history bytes a scan would have read, per second
         ("scan_equivalent_GBps" if args.index else "scan_GBps"):
             round(bytes_mean * steps_n / gpu_s / 1e9, 1),
-        "hbm_frac": None if args.index else
+        "hbm_frac": None if (args.index or args.ngram) else
             round(bytes_mean * steps_n / gpu_s / 1e9 / HBM_PEAK_GBPS, 4),
     }
+    if args.ngram:
+        # a different drafter: no history bytes are read per step
+        rec["metric"] = METRIC_NGRAM
+        del rec["scan_GBps"]
+        rec["config"]["n_min"], rec["config"]["n_max"] = nparams.n_min, nparams.n_max
+        rec["mean_draft_tokens"] = round(float(np.mean([f[1] for f in first_drafts])), 3)
     if not args.no_cpu_baseline:
         import oracle
         hs = [h.copy() for h in start.histories]
         n, parity, t_start = 0, True, time.perf_counter()
+        op = oracle.NgramParams()
         while n < steps_n and time.perf_counter() - t_start < args.cpu_seconds:
-            od, ol, om, _ = oracle.draft(hs, start.n_min, start.n_max, start.k_max)
+            if args.ngram:
+                od, ol, om = oracle.ngram_draft(op, hs, start.k_max)
+            else:
+                od, ol, om, _ = oracle.draft(hs, start.n_min, start.n_max, start.k_max)
             gd, gl, gm = first_drafts[n]
             parity &= (np.array_equal(od, gd) and np.array_equal(ol, gl)
                        and np.array_equal(om, gm))

@@ -128,7 +128,10 @@ pld_status pld_configure(pld_ctx *ctx, int32_t tile_tokens, int32_t fused_gather
  * unchanged and sets the sticky flag (PLD_ECAPACITY / PLD_EINVAL at
  * pld_sync). batch == 0 is a no-op. With an index (pld_create_indexed) the
  * n-grams that the append makes draftable are inserted first, in a second
- * kernel on the same stream.
+ * kernel on the same stream. With a successor-count cache
+ * (pld_create_ngram) the appended tokens' n-grams are counted in the same
+ * launch as the copy when 0 < tokens_stride <= 1024, otherwise in a kernel
+ * before it.
  * Errors: PLD_EINVAL (no store, batch outside [0, max_batch], null pointers,
  * negative stride), PLD_EHIP.
  */
@@ -406,6 +409,69 @@ pld_status pld_control(pld_ctx *ctx, const pld_control_params *params, const int
                        const double *round_time, const int32_t *lookup_len,
                        const int32_t *lookup_match, double *state, int32_t batch,
                        int32_t *out_source, double *out_rates, hipStream_t stream);
+
+/*
+ * Successor-count n-gram drafting (llama.cpp page, the section on what
+ * prompt lookup decoding is: its context cache).
+ *
+ * The drafter keeps statistics of the n-grams of sizes 1..4 of the current
+ * token stream and of the tokens that followed them, and builds a draft one
+ * token at a time, each token one lookup of the tokens before it, proposing
+ * a context's most frequent successor when fixed thresholds pass (the
+ * page's example: a 4-gram seen at least once whose most frequent successor
+ * holds at least half of its occurrences). Computed per request, for each
+ * draft token s < k_max:
+ *  - the context of length n is the last n tokens of the history followed
+ *    by draft tokens 0..s-1 (drafted tokens are never counted);
+ *  - n runs from n_max down to n_min; its statistics are over the history
+ *    h[0..L): count = the positions i in [n, L) with h[i-n..i) equal to the
+ *    context, and the most frequent h[i] among them (the smaller token, as
+ *    a signed integer, on a tie) with `top` occurrences;
+ *  - the first n with count >= max(1, min_count[n-1]) and
+ *    100 * top >= min_percent[n-1] * count proposes that token;
+ *  - the draft ends at the first token no length proposes.
+ * Defaults (pld_ngram_params_default): n 1..4, min_count 1 and min_percent
+ * 50 for every length (the page gives these for the 4-gram).
+ */
+#define PLD_NGRAM_MAX_N 4
+
+typedef struct pld_ngram_params {
+    int32_t n_min;                        /* shortest context tried, >= 1 */
+    int32_t n_max;                        /* longest, <= the context's cache */
+    int32_t min_count[PLD_NGRAM_MAX_N];   /* per length n at [n-1], >= 0 */
+    int32_t min_percent[PLD_NGRAM_MAX_N]; /* per length n at [n-1], 0..100 */
+} pld_ngram_params;
+
+/* Fills *params with the defaults above. Errors: PLD_EINVAL (null). */
+pld_status pld_ngram_params_default(pld_ngram_params *params);
+
+/*
+ * pld_create with a store (own_store = 1) and a successor-count cache over
+ * it for context lengths 1..n_max (1 <= n_max <= PLD_NGRAM_MAX_N).
+ * pld_append keeps it current (O(n_max) work per appended token) and
+ * pld_store_reset empties it. Per request and length: a table of 32-byte
+ * n-gram slots and one of 8-byte successor-pair slots, each a power of two
+ * >= max(16, 2 * max_len) slots (1.34 GB for 64 requests of 49,152 tokens
+ * and n_max 4). A context has either this cache or an index, not both.
+ * Errors: as pld_create; PLD_EINVAL for n_max out of range.
+ */
+pld_status pld_create_ngram(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t n_max);
+
+/*
+ * Drafts for the first `batch` rows of the context's store from its
+ * successor-count cache, by the rule above. One wavefront per request looks
+ * up all lengths of a draft token in one round trip; results are exact
+ * (n-grams are compared by their tokens, never by hash alone).
+ *  params: host pointer; n_max at most the cache's.
+ *  out_draft: device int32[batch * k_max], row-major, -1 past out_len[b].
+ *  out_len: device int32[batch], the draft lengths.
+ *  out_levels: device int32[batch * k_max] or NULL: the context length
+ *              behind each draft token, 0 past out_len[b].
+ * Errors: PLD_EINVAL (no cache, bad params, sizes, pointers), PLD_EHIP.
+ */
+pld_status pld_draft_ngram(pld_ctx *ctx, const pld_ngram_params *params, int32_t batch,
+                           int32_t k_max, int32_t *out_draft, int32_t *out_len,
+                           int32_t *out_levels, hipStream_t stream);
 
 /*
  * Wait for the stream, then report and clear the sticky device-side flag:

@@ -33,6 +33,7 @@ EXPORTS = ("pld_create", "pld_create_indexed", "pld_destroy", "pld_configure", "
            "pld_draft_store", "pld_append_draft_store",
            "pld_fuse_params_default",
            "pld_fuse", "pld_draft_fuse_batch", "pld_control_params_default", "pld_control",
+           "pld_ngram_params_default", "pld_create_ngram", "pld_draft_ngram",
            "pld_sync", "pld_strerror",
            "pld_last_error")
 
@@ -58,6 +59,16 @@ class PldControlParams(ctypes.Structure):
 
 PLD_CONTROL_STATE_WORDS = 11
 PLD_SOURCE_PLAIN, PLD_SOURCE_MTP, PLD_SOURCE_LOOKUP = 0, 1, 2
+
+PLD_NGRAM_MAX_N = 4
+
+
+class PldNgramParams(ctypes.Structure):
+    """pld_ngram_params (include/pld.h); pld_ngram_params_default() gives the
+    llama.cpp page's context-cache thresholds for every length."""
+    _fields_ = [("n_min", ctypes.c_int32), ("n_max", ctypes.c_int32),
+                ("min_count", ctypes.c_int32 * PLD_NGRAM_MAX_N),
+                ("min_percent", ctypes.c_int32 * PLD_NGRAM_MAX_N)]
 
 
 class PldError(RuntimeError):
@@ -99,6 +110,9 @@ def load(path: str = LIB_PATH):
         "pld_control_params_default": [ctypes.POINTER(PldControlParams)],
         "pld_control": [vp, ctypes.POINTER(PldControlParams), vp, vp, vp, vp, vp, i32, vp, vp,
                         vp],
+        "pld_ngram_params_default": [ctypes.POINTER(PldNgramParams)],
+        "pld_create_ngram": [ctypes.POINTER(vp), i32, i32, i32],
+        "pld_draft_ngram": [vp, ctypes.POINTER(PldNgramParams), i32, i32, vp, vp, vp, vp],
         "pld_sync": [vp, vp],
     }
     for name, args in sig.items():
@@ -180,6 +194,14 @@ def pld_create_indexed(max_batch: int, max_len: int, n_min: int, n_max: int) -> 
     ctx = ctypes.c_void_p()
     _check("pld_create_indexed", load().pld_create_indexed(
         ctypes.byref(ctx), int(max_batch), int(max_len), int(n_min), int(n_max)))
+    return ctx.value
+
+
+def pld_create_ngram(max_batch: int, max_len: int, n_max: int = PLD_NGRAM_MAX_N) -> int:
+    """A context with a history store and a successor-count cache over it."""
+    ctx = ctypes.c_void_p()
+    _check("pld_create_ngram", load().pld_create_ngram(
+        ctypes.byref(ctx), int(max_batch), int(max_len), int(n_max)))
     return ctx.value
 
 
@@ -339,6 +361,23 @@ def pld_control(ctx: int, params: PldControlParams, accepted, round_time, lookup
         _dev_ptr(round_time, "round_time", f64), _dev_ptr(lookup_len, "lookup_len", i32),
         _dev_ptr(lookup_match, "lookup_match", i32), _dev_ptr(state, "state", f64), int(batch),
         _dev_ptr(out_source, "out_source", i32), _dev_ptr(out_rates, "out_rates", f64),
+        _stream(stream)))
+
+
+def pld_ngram_params_default() -> PldNgramParams:
+    p = PldNgramParams()
+    _check("pld_ngram_params_default", load().pld_ngram_params_default(ctypes.byref(p)))
+    return p
+
+
+def pld_draft_ngram(ctx: int, params: PldNgramParams, batch: int, k_max: int, out_draft,
+                    out_len, out_levels=None, stream=None) -> None:
+    """Draft the store's first `batch` rows from the successor-count cache
+    (include/pld.h)."""
+    i32 = _i32()
+    _check("pld_draft_ngram", load().pld_draft_ngram(
+        ctx, ctypes.byref(params), int(batch), int(k_max), _dev_ptr(out_draft, "out_draft", i32),
+        _dev_ptr(out_len, "out_len", i32), _dev_ptr(out_levels, "out_levels", i32),
         _stream(stream)))
 
 

@@ -29,7 +29,8 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
 
 def sources():
     return [os.path.join(CSRC, "pld_kernels.hip"), os.path.join(CSRC, "pld_index.hip"),
-            os.path.join(CSRC, "pld_control.hip"), os.path.join(CSRC, "pld_api.cpp")]
+            os.path.join(CSRC, "pld_control.hip"), os.path.join(CSRC, "pld_ngram.hip"),
+            os.path.join(CSRC, "pld_api.cpp")]
 
 
 def build(verbose: bool = False) -> str:

@@ -32,6 +32,11 @@ struct pld_ctx {
     int32_t index_lo, index_hi; // indexed lengths
     int32_t index_chunks;       // workgroups per request for an append's inserts
     uint32_t index_fp_mask;     // fingerprint bits kept
+    unsigned long long *ngram_grams;  // successor-count cache: gram slots, or null
+    unsigned long long *ngram_pairs;  // and pair slots
+    int64_t ngram_cap;                // slots per (request, length) table
+    int32_t ngram_n_max;              // context lengths 1..ngram_n_max
+    int32_t ngram_chunks;             // workgroups per request for a large append
 };
 
 namespace {
@@ -65,6 +70,8 @@ void release(pld_ctx *c)
     if (c->store_len) (void)hipFree(c->store_len);
     if (c->store_rows) (void)hipFree(c->store_rows);
     if (c->index) (void)hipFree(c->index);
+    if (c->ngram_grams) (void)hipFree(c->ngram_grams);
+    if (c->ngram_pairs) (void)hipFree(c->ngram_pairs);
     delete c;
 }
 
@@ -175,6 +182,21 @@ pld::IndexArgs index_args(pld_ctx *ctx)
     return a;
 }
 
+pld::NgramArgs ngram_args(pld_ctx *ctx)
+{
+    pld::NgramArgs a;
+    a.grams = ctx->ngram_grams;
+    a.pairs = ctx->ngram_pairs;
+    a.cap = ctx->ngram_cap;
+    a.n_max = ctx->ngram_n_max;
+    a.store = ctx->store;
+    a.pitch = ctx->pitch;
+    a.lengths = ctx->store_len;
+    a.max_len = ctx->max_len;
+    a.err = ctx->err;
+    return a;
+}
+
 // Checks a fusion step's arguments and fills `a`; PLD_OK or the failure.
 pld_status fuse_args(pld_ctx *ctx, const pld_fuse_params *params, const int32_t *lookup,
                      int32_t lookup_k, const int32_t *lookup_len, const int32_t *lookup_match,
@@ -234,7 +256,7 @@ pld_status fuse_args(pld_ctx *ctx, const pld_fuse_params *params, const int32_t 
 
 // Creates a context; index_lo > 0 adds an n-gram index over the store.
 pld_status create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t own_store,
-                  int32_t index_lo, int32_t index_hi)
+                  int32_t index_lo, int32_t index_hi, int32_t ngram_n_max = 0)
 {
     if (!out)
         return fail(PLD_EINVAL, "out is null");
@@ -298,9 +320,30 @@ pld_status create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t own
         const int64_t chunks = max_len / 8192;
         c->index_chunks = (int32_t)(chunks < 1 ? 1 : (chunks > 16 ? 16 : chunks));
     }
+    if (ngram_n_max > 0) {
+        int64_t cap = 16;
+        while (cap < 2 * (int64_t)max_len)
+            cap <<= 1;
+        const double slots = (double)nb * (double)ngram_n_max * (double)cap;
+        const size_t n = (size_t)nb * (size_t)ngram_n_max * (size_t)cap;
+        if (slots * 40.0 > 9.0e18 ||
+            hipMalloc((void **)&c->ngram_grams, n * 32) != hipSuccess ||
+            hipMalloc((void **)&c->ngram_pairs, n * 8) != hipSuccess) {
+            (void)hipGetLastError();
+            release(c);
+            return fail(PLD_ENOMEM, "device allocation of the successor-count cache (%.0f MB) "
+                        "failed", slots * 40.0 / 1e6);
+        }
+        c->ngram_cap = cap;
+        c->ngram_n_max = ngram_n_max;
+        const int64_t chunks = max_len / 8192;
+        c->ngram_chunks = (int32_t)(chunks < 1 ? 1 : (chunks > 16 ? 16 : chunks));
+    }
     e = hipMemset(c->slots, 0, nb * sizeof(pld::ReqSlot));
     if (e == hipSuccess && c->index)
         e = pld::launch_index_clear(index_args(c), max_batch, nullptr);
+    if (e == hipSuccess && c->ngram_grams)
+        e = pld::launch_ngram_clear(ngram_args(c), max_batch, nullptr);
     if (e == hipSuccess) e = hipMemset(c->err, 0, sizeof(unsigned int));
     if (e == hipSuccess) e = hipMemset(c->zero16, 0, sizeof(int4));
     if (e == hipSuccess && own_store) {
@@ -342,6 +385,13 @@ pld_status pld_create_indexed(pld_ctx **out, int32_t max_batch, int32_t max_len,
         return fail(PLD_EINVAL, "need 1 <= n_min <= n_max <= %d (got n_min=%d n_max=%d)",
                     PLD_N_MAX_LIMIT, n_min, n_max);
     return create(out, max_batch, max_len, 1, n_min, n_max);
+}
+
+pld_status pld_create_ngram(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t n_max)
+{
+    if (n_max < 1 || n_max > PLD_NGRAM_MAX_N)
+        return fail(PLD_EINVAL, "need 1 <= n_max <= %d (got %d)", PLD_NGRAM_MAX_N, n_max);
+    return create(out, max_batch, max_len, 1, 0, 0, n_max);
 }
 
 pld_status pld_destroy(pld_ctx *ctx)
@@ -396,7 +446,19 @@ pld_status pld_append(pld_ctx *ctx, const int32_t *tokens, int64_t tokens_stride
     a.max_len = ctx->max_len;
     a.err = ctx->err;
     hipError_t e = hipSuccess;
-    if (ctx->index && tokens_stride > 0 && tokens_stride <= kSmallAppend) {
+    if (ctx->ngram_grams) {
+        if (tokens_stride > 0 && tokens_stride <= kSmallAppend) {
+            // counts and copy in one workgroup per request
+            e = pld::launch_append_ngram(ngram_args(ctx), tokens, tokens_stride, counts, batch,
+                                         stream);
+        } else {
+            // before the copy: it reads the old length and the store
+            e = pld::launch_ngram_insert(ngram_args(ctx), tokens, tokens_stride, counts, batch,
+                                         ctx->ngram_chunks, stream);
+            if (e == hipSuccess)
+                e = pld::launch_append(a, batch, stream);
+        }
+    } else if (ctx->index && tokens_stride > 0 && tokens_stride <= kSmallAppend) {
         // rows of at most kSmallAppend tokens (a decode loop's appends):
         // inserts and copy in one workgroup per request
         e = pld::launch_append_indexed(index_args(ctx), tokens, tokens_stride, counts, batch,
@@ -434,6 +496,8 @@ pld_status pld_store_reset(pld_ctx *ctx, hipStream_t stream)
     hipError_t e = pld::launch_fill(ctx->store_len, ctx->max_batch, 0, stream);
     if (e == hipSuccess && ctx->index)
         e = pld::launch_index_clear(index_args(ctx), ctx->max_batch, stream);
+    if (e == hipSuccess && ctx->ngram_grams)
+        e = pld::launch_ngram_clear(ngram_args(ctx), ctx->max_batch, stream);
     if (e != hipSuccess)
         return hip_fail(e, "store reset launch");
     return PLD_OK;
@@ -485,6 +549,68 @@ pld_status pld_append_draft_store(pld_ctx *ctx, const int32_t *tokens, int64_t t
                                                     out_len, out_match, out_pos, stream);
     if (e != hipSuccess)
         return hip_fail(e, "append-draft launch");
+    return PLD_OK;
+}
+
+pld_status pld_ngram_params_default(pld_ngram_params *params)
+{
+    if (!params)
+        return fail(PLD_EINVAL, "params is null");
+    params->n_min = 1;
+    params->n_max = PLD_NGRAM_MAX_N;
+    for (int i = 0; i < PLD_NGRAM_MAX_N; ++i) {
+        params->min_count[i] = 1;
+        params->min_percent[i] = 50;
+    }
+    return PLD_OK;
+}
+
+pld_status pld_draft_ngram(pld_ctx *ctx, const pld_ngram_params *params, int32_t batch,
+                           int32_t k_max, int32_t *out_draft, int32_t *out_len,
+                           int32_t *out_levels, hipStream_t stream)
+{
+    if (!ctx)
+        return fail(PLD_EINVAL, "ctx is null");
+    if (!ctx->ngram_grams)
+        return fail(PLD_EINVAL, "context has no successor-count cache (see pld_create_ngram)");
+    if (!params)
+        return fail(PLD_EINVAL, "params is null");
+    const pld_ngram_params &p = *params;
+    if (p.n_min < 1 || p.n_max < p.n_min || p.n_max > ctx->ngram_n_max)
+        return fail(PLD_EINVAL, "need 1 <= n_min <= n_max <= %d, the cached lengths "
+                    "(got n_min=%d n_max=%d)", ctx->ngram_n_max, p.n_min, p.n_max);
+    for (int i = 0; i < PLD_NGRAM_MAX_N; ++i) {
+        if (p.min_count[i] < 0 || p.min_percent[i] < 0 || p.min_percent[i] > 100)
+            return fail(PLD_EINVAL, "need min_count >= 0 and 0 <= min_percent <= 100 "
+                        "(length %d: %d, %d)", i + 1, p.min_count[i], p.min_percent[i]);
+    }
+    if (k_max < 1)
+        return fail(PLD_EINVAL, "k_max must be >= 1 (got %d)", k_max);
+    if (batch < 0 || batch > ctx->max_batch)
+        return fail(PLD_EINVAL, "batch %d outside [0, max_batch=%d]", batch, ctx->max_batch);
+    if (batch == 0)
+        return PLD_OK;
+    if (!out_draft || !out_len)
+        return fail(PLD_EINVAL, "null buffer pointer");
+    if (((uintptr_t)out_draft | (uintptr_t)out_len | (uintptr_t)out_levels) & 3u)
+        return fail(PLD_EINVAL, "outputs must be 4-byte aligned");
+    if ((int64_t)batch * k_max > INT64_MAX / 4)
+        return fail(PLD_EINVAL, "batch * k_max too large");
+    pld::NgramDraftArgs d;
+    d.n_min = p.n_min;
+    d.n_max = p.n_max;
+    for (int i = 0; i < PLD_NGRAM_MAX_N; ++i) {
+        d.min_count[i] = p.min_count[i];
+        d.min_percent[i] = p.min_percent[i];
+    }
+    d.batch = batch;
+    d.k_max = k_max;
+    d.out_draft = out_draft;
+    d.out_len = out_len;
+    d.out_levels = out_levels;
+    hipError_t e = pld::launch_ngram_draft(ngram_args(ctx), d, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "n-gram draft launch");
     return PLD_OK;
 }
 

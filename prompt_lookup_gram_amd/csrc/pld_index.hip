@@ -42,6 +42,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pld_device.h"
 #include "pld_kernels.h"
 
 namespace pld {
@@ -51,26 +52,6 @@ namespace {
 typedef unsigned long long u64;
 constexpr int kWave = 64;
 
-// Hash of an n-gram read backwards from its end: one step per token, then a
-// final mix (a 64-bit multiply-xorshift finaliser).
-__device__ __forceinline__ u64 hstep(u64 h, int32_t t)
-{
-    h ^= (uint32_t)t;
-    h *= 0x9e3779b97f4a7c15ull;
-    return h ^ (h >> 29);
-}
-
-__device__ __forceinline__ u64 hfinal(u64 h)
-{
-    h ^= h >> 33;
-    h *= 0xff51afd7ed558ccdull;
-    h ^= h >> 33;
-    h *= 0xc4ceb9fe1a85ec53ull;
-    return h ^ (h >> 33);
-}
-
-constexpr u64 kHashSeed = 0x243f6a8885a308d3ull;
-
 // LDS tokens for the n-grams of a one-workgroup append (appends up to 1,024
 // tokens plus the 63 before them; longer ones hash from memory).
 constexpr int kAppendWindow = 1024 + 64;
@@ -79,20 +60,6 @@ __device__ __forceinline__ u64 *table_of(const IndexArgs &a, int b, int n)
 {
     return a.table + ((int64_t)b * (a.n_hi - a.n_lo + 1) + (n - a.n_lo)) * a.cap;
 }
-
-// Token q of request b during an append: from the store below the old
-// length, from the append's source row above it.
-struct AppendView {
-    const int32_t *store_row;
-    const int32_t *src;
-    int32_t old_len;
-    __device__ __forceinline__ int32_t at(int64_t q) const
-    {
-        // one load from whichever buffer holds q
-        const int32_t *p = q < old_len ? store_row + q : src + (q - old_len);
-        return *p;
-    }
-};
 
 // Inserts the end e of an n-gram with hash f into its table: into the
 // first slot of the probe sequence that is empty or holds the fingerprint.

@@ -98,6 +98,34 @@ struct IndexArgs {
     unsigned int *err;
 };
 
+// The context store's successor-count cache (pld_ngram.hip): per request
+// and context length n in [1, n_max], a gram table of `cap` 32-byte slots
+// (count << 32 | end + 1, top successor, the n tokens) and a pair table of
+// `cap` 8-byte slots (count << 32 | end + 1) for the (n + 1)-grams.
+struct NgramArgs {
+    unsigned long long *grams;  // [max_batch][n_max][cap][4]
+    unsigned long long *pairs;  // [max_batch][n_max][cap]
+    int64_t cap;                // a power of two >= max(16, 2 * max_len)
+    int32_t n_max;              // context lengths kept: 1..n_max (<= 4)
+    int32_t *store;             // [max_batch * pitch]
+    int64_t pitch;
+    int32_t *lengths;           // [max_batch]
+    int32_t max_len;
+    unsigned int *err;
+};
+
+// One drafting call from the cache: thresholds per context length n at
+// index n - 1.
+struct NgramDraftArgs {
+    int32_t n_min, n_max;
+    int32_t min_count[4];
+    int32_t min_percent[4];
+    int32_t batch, k_max;
+    int32_t *out_draft;   // [batch, k_max]
+    int32_t *out_len;     // [batch]
+    int32_t *out_levels;  // [batch, k_max] or null
+};
+
 // The online cost/benefit controller (pld_control.hip).
 struct ControlArgs {
     double alpha, beta, margin, prior_accept, prior_time;
@@ -137,6 +165,13 @@ hipError_t launch_index_draft(const IndexArgs &a, int32_t batch, int32_t n_min, 
                               int32_t *out_match, int32_t *out_pos, hipStream_t s);
 hipError_t launch_index_clear(const IndexArgs &a, int32_t batch, hipStream_t s);
 hipError_t launch_control(const ControlArgs &a, hipStream_t s);
+hipError_t launch_ngram_insert(const NgramArgs &a, const int32_t *tokens, int64_t tokens_stride,
+                               const int32_t *counts, int32_t batch, int32_t chunks,
+                               hipStream_t s);
+hipError_t launch_append_ngram(const NgramArgs &a, const int32_t *tokens, int64_t tokens_stride,
+                               const int32_t *counts, int32_t batch, hipStream_t s);
+hipError_t launch_ngram_draft(const NgramArgs &a, const NgramDraftArgs &d, hipStream_t s);
+hipError_t launch_ngram_clear(const NgramArgs &a, int32_t batch, hipStream_t s);
 
 }  // namespace pld
 

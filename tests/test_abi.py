@@ -113,3 +113,23 @@ def test_control_params_default():
     assert (p.alpha, p.beta, p.margin, p.prior_accept, p.prior_time, p.mtp_tokens) == \
         (0.1, 0.1, 1.05, 0.5, 1.0, 3)
     assert list(p.bucket_edge) == [6, 8, 12]
+
+
+def test_ngram_params_default():
+    """llama.cpp page, its context cache: n-grams of sizes 1 to 4; the
+    4-gram seen at least once with its top successor at half or more,
+    used for every length."""
+    p = B.pld_ngram_params_default()
+    assert (p.n_min, p.n_max) == (1, 4)
+    assert list(p.min_count) == [1, 1, 1, 1] and list(p.min_percent) == [50, 50, 50, 50]
+
+
+def test_create_ngram_rejects_bad_lengths_before_any_hip_call():
+    ctx = ctypes.c_void_p()
+    for n_max in (0, 5, -1):
+        assert _raw("pld_create_ngram", ctypes.byref(ctx), 4, 100, n_max) == B.PLD_EINVAL
+        assert "n_max" in B.pld_last_error()
+    p = B.pld_ngram_params_default()
+    assert _raw("pld_draft_ngram", None, ctypes.byref(p), 1, 16, None, None, None,
+                None) == B.PLD_EINVAL
+    assert "ctx is null" in B.pld_last_error()
