@@ -146,9 +146,9 @@ def main():
     dev = torch.device("cuda:0")
     B.load()
 
-    if args.ngram and (args.index or args.append_draft or args.fuse != "none"):
+    if args.ngram and (args.index or args.fuse != "none"):
         print("--ngram drafts from the successor-count cache: it does not combine with "
-              "--index, --append-draft or --fuse", file=sys.stderr)
+              "--index or --fuse", file=sys.stderr)
         sys.exit(2)
     if args.config == 5:
         return bench_stream(args, torch, B, wl, dev)
@@ -709,9 +709,13 @@ def bench_stream(args, torch, B, wl, dev):
             draft()
             control()
             for step in range(steps_n - 1):
-                B.pld_append_draft_store(ctx, toks_d[step], width, cnts_d[step], nb,
-                                         start.n_min, start.n_max, start.k_max, out[0], out[1],
-                                         out[2])
+                if args.ngram:
+                    B.pld_append_draft_ngram(ctx, toks_d[step], width, cnts_d[step], nb,
+                                             nparams, start.k_max, out[0], out[1], levels)
+                else:
+                    B.pld_append_draft_store(ctx, toks_d[step], width, cnts_d[step], nb,
+                                             start.n_min, start.n_max, start.k_max, out[0],
+                                             out[1], out[2])
                 control()
             B.pld_append(ctx, toks_d[steps_n - 1], width, cnts_d[steps_n - 1], nb)
         else:

@@ -449,9 +449,9 @@ pld_status pld_ngram_params_default(pld_ngram_params *params);
  * pld_create with a store (own_store = 1) and a successor-count cache over
  * it for context lengths 1..n_max (1 <= n_max <= PLD_NGRAM_MAX_N).
  * pld_append keeps it current (O(n_max) work per appended token) and
- * pld_store_reset empties it. Per request and length: a table of 32-byte
- * n-gram slots and one of 8-byte successor-pair slots, each a power of two
- * >= max(16, 2 * max_len) slots (1.34 GB for 64 requests of 49,152 tokens
+ * pld_store_reset empties it. Per request and length: a table of n-gram
+ * slots and one of successor-pair slots, 32 bytes each, each a power of two
+ * >= max(16, 2 * max_len) slots (2.15 GB for 64 requests of 49,152 tokens
  * and n_max 4). A context has either this cache or an index, not both.
  * Errors: as pld_create; PLD_EINVAL for n_max out of range.
  */
@@ -472,6 +472,23 @@ pld_status pld_create_ngram(pld_ctx **out, int32_t max_batch, int32_t max_len, i
 pld_status pld_draft_ngram(pld_ctx *ctx, const pld_ngram_params *params, int32_t batch,
                            int32_t k_max, int32_t *out_draft, int32_t *out_len,
                            int32_t *out_levels, hipStream_t stream);
+
+/*
+ * One decode step on a successor-count context: pld_append (tokens,
+ * tokens_stride, counts, batch as there), then pld_draft_ngram of the first
+ * `batch` rows (params, k_max and outputs as there). With
+ * 0 < tokens_stride <= 1024 both steps run in one launch, one workgroup per
+ * request (the draft starts from the appended tokens it already holds);
+ * otherwise as the two calls. Results are the same either way. A rejected
+ * append leaves its row as it was, and that row is drafted as it stands.
+ * All arguments are checked before anything is enqueued.
+ * Errors: those of pld_append and pld_draft_ngram.
+ */
+pld_status pld_append_draft_ngram(pld_ctx *ctx, const int32_t *tokens, int64_t tokens_stride,
+                                  const int32_t *counts, int32_t batch,
+                                  const pld_ngram_params *params, int32_t k_max,
+                                  int32_t *out_draft, int32_t *out_len, int32_t *out_levels,
+                                  hipStream_t stream);
 
 /*
  * Wait for the stream, then report and clear the sticky device-side flag:

@@ -34,6 +34,7 @@ EXPORTS = ("pld_create", "pld_create_indexed", "pld_destroy", "pld_configure", "
            "pld_fuse_params_default",
            "pld_fuse", "pld_draft_fuse_batch", "pld_control_params_default", "pld_control",
            "pld_ngram_params_default", "pld_create_ngram", "pld_draft_ngram",
+           "pld_append_draft_ngram",
            "pld_sync", "pld_strerror",
            "pld_last_error")
 
@@ -113,6 +114,8 @@ def load(path: str = LIB_PATH):
         "pld_ngram_params_default": [ctypes.POINTER(PldNgramParams)],
         "pld_create_ngram": [ctypes.POINTER(vp), i32, i32, i32],
         "pld_draft_ngram": [vp, ctypes.POINTER(PldNgramParams), i32, i32, vp, vp, vp, vp],
+        "pld_append_draft_ngram": [vp, vp, i64, vp, i32, ctypes.POINTER(PldNgramParams), i32,
+                                   vp, vp, vp, vp],
         "pld_sync": [vp, vp],
     }
     for name, args in sig.items():
@@ -377,6 +380,19 @@ def pld_draft_ngram(ctx: int, params: PldNgramParams, batch: int, k_max: int, ou
     i32 = _i32()
     _check("pld_draft_ngram", load().pld_draft_ngram(
         ctx, ctypes.byref(params), int(batch), int(k_max), _dev_ptr(out_draft, "out_draft", i32),
+        _dev_ptr(out_len, "out_len", i32), _dev_ptr(out_levels, "out_levels", i32),
+        _stream(stream)))
+
+
+def pld_append_draft_ngram(ctx: int, tokens, tokens_stride: int, counts, batch: int,
+                           params: PldNgramParams, k_max: int, out_draft, out_len,
+                           out_levels=None, stream=None) -> None:
+    """pld_append, then pld_draft_ngram of the store's first `batch` rows, in
+    one launch for 0 < tokens_stride <= 1024 (include/pld.h)."""
+    i32 = _i32()
+    _check("pld_append_draft_ngram", load().pld_append_draft_ngram(
+        ctx, _dev_ptr(tokens, "tokens", i32), int(tokens_stride), _dev_ptr(counts, "counts", i32),
+        int(batch), ctypes.byref(params), int(k_max), _dev_ptr(out_draft, "out_draft", i32),
         _dev_ptr(out_len, "out_len", i32), _dev_ptr(out_levels, "out_levels", i32),
         _stream(stream)))
 

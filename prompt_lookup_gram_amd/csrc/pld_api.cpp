@@ -326,13 +326,13 @@ pld_status create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t own
             cap <<= 1;
         const double slots = (double)nb * (double)ngram_n_max * (double)cap;
         const size_t n = (size_t)nb * (size_t)ngram_n_max * (size_t)cap;
-        if (slots * 40.0 > 9.0e18 ||
+        if (slots * 64.0 > 9.0e18 ||
             hipMalloc((void **)&c->ngram_grams, n * 32) != hipSuccess ||
-            hipMalloc((void **)&c->ngram_pairs, n * 8) != hipSuccess) {
+            hipMalloc((void **)&c->ngram_pairs, n * 32) != hipSuccess) {
             (void)hipGetLastError();
             release(c);
             return fail(PLD_ENOMEM, "device allocation of the successor-count cache (%.0f MB) "
-                        "failed", slots * 40.0 / 1e6);
+                        "failed", slots * 64.0 / 1e6);
         }
         c->ngram_cap = cap;
         c->ngram_n_max = ngram_n_max;
@@ -565,9 +565,11 @@ pld_status pld_ngram_params_default(pld_ngram_params *params)
     return PLD_OK;
 }
 
-pld_status pld_draft_ngram(pld_ctx *ctx, const pld_ngram_params *params, int32_t batch,
-                           int32_t k_max, int32_t *out_draft, int32_t *out_len,
-                           int32_t *out_levels, hipStream_t stream)
+// Checks a successor-count draft's arguments and fills `d`; PLD_OK or the
+// failure.
+pld_status ngram_draft_args(pld_ctx *ctx, const pld_ngram_params *params, int32_t batch,
+                            int32_t k_max, int32_t *out_draft, int32_t *out_len,
+                            int32_t *out_levels, pld::NgramDraftArgs &d)
 {
     if (!ctx)
         return fail(PLD_EINVAL, "ctx is null");
@@ -588,15 +590,12 @@ pld_status pld_draft_ngram(pld_ctx *ctx, const pld_ngram_params *params, int32_t
         return fail(PLD_EINVAL, "k_max must be >= 1 (got %d)", k_max);
     if (batch < 0 || batch > ctx->max_batch)
         return fail(PLD_EINVAL, "batch %d outside [0, max_batch=%d]", batch, ctx->max_batch);
-    if (batch == 0)
-        return PLD_OK;
-    if (!out_draft || !out_len)
+    if (batch > 0 && (!out_draft || !out_len))
         return fail(PLD_EINVAL, "null buffer pointer");
     if (((uintptr_t)out_draft | (uintptr_t)out_len | (uintptr_t)out_levels) & 3u)
         return fail(PLD_EINVAL, "outputs must be 4-byte aligned");
     if ((int64_t)batch * k_max > INT64_MAX / 4)
         return fail(PLD_EINVAL, "batch * k_max too large");
-    pld::NgramDraftArgs d;
     d.n_min = p.n_min;
     d.n_max = p.n_max;
     for (int i = 0; i < PLD_NGRAM_MAX_N; ++i) {
@@ -608,9 +607,50 @@ pld_status pld_draft_ngram(pld_ctx *ctx, const pld_ngram_params *params, int32_t
     d.out_draft = out_draft;
     d.out_len = out_len;
     d.out_levels = out_levels;
+    return PLD_OK;
+}
+
+pld_status pld_draft_ngram(pld_ctx *ctx, const pld_ngram_params *params, int32_t batch,
+                           int32_t k_max, int32_t *out_draft, int32_t *out_len,
+                           int32_t *out_levels, hipStream_t stream)
+{
+    pld::NgramDraftArgs d;
+    pld_status st = ngram_draft_args(ctx, params, batch, k_max, out_draft, out_len, out_levels, d);
+    if (st != PLD_OK || batch == 0)
+        return st;
     hipError_t e = pld::launch_ngram_draft(ngram_args(ctx), d, stream);
     if (e != hipSuccess)
         return hip_fail(e, "n-gram draft launch");
+    return PLD_OK;
+}
+
+pld_status pld_append_draft_ngram(pld_ctx *ctx, const int32_t *tokens, int64_t tokens_stride,
+                                  const int32_t *counts, int32_t batch,
+                                  const pld_ngram_params *params, int32_t k_max,
+                                  int32_t *out_draft, int32_t *out_len, int32_t *out_levels,
+                                  hipStream_t stream)
+{
+    // every argument of both steps is checked before anything is enqueued
+    pld::NgramDraftArgs d;
+    pld_status st = ngram_draft_args(ctx, params, batch, k_max, out_draft, out_len, out_levels, d);
+    if (st != PLD_OK)
+        return st;
+    if (tokens_stride < 0)
+        return fail(PLD_EINVAL, "tokens_stride must be >= 0");
+    if (batch == 0)
+        return PLD_OK;
+    if (!tokens || !counts)
+        return fail(PLD_EINVAL, "null buffer pointer");
+    if (tokens_stride == 0 || tokens_stride > kSmallAppend) {
+        st = pld_append(ctx, tokens, tokens_stride, counts, batch, stream);
+        if (st != PLD_OK)
+            return st;
+        return pld_draft_ngram(ctx, params, batch, k_max, out_draft, out_len, out_levels, stream);
+    }
+    hipError_t e = pld::launch_append_draft_ngram(ngram_args(ctx), tokens, tokens_stride, counts,
+                                                  d, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "n-gram append-draft launch");
     return PLD_OK;
 }
 

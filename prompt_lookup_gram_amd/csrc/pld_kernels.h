@@ -99,12 +99,12 @@ struct IndexArgs {
 };
 
 // The context store's successor-count cache (pld_ngram.hip): per request
-// and context length n in [1, n_max], a gram table of `cap` 32-byte slots
-// (count << 32 | end + 1, top successor, the n tokens) and a pair table of
-// `cap` 8-byte slots (count << 32 | end + 1) for the (n + 1)-grams.
+// and context length n in [1, n_max], a gram table and a pair table of `cap`
+// 32-byte slots each (count << 32 | end + 1, then the top successor or the
+// 5th token, then 4 tokens) for the n-grams and the (n + 1)-grams.
 struct NgramArgs {
     unsigned long long *grams;  // [max_batch][n_max][cap][4]
-    unsigned long long *pairs;  // [max_batch][n_max][cap]
+    unsigned long long *pairs;  // [max_batch][n_max][cap][4]
     int64_t cap;                // a power of two >= max(16, 2 * max_len)
     int32_t n_max;              // context lengths kept: 1..n_max (<= 4)
     int32_t *store;             // [max_batch * pitch]
@@ -171,6 +171,9 @@ hipError_t launch_ngram_insert(const NgramArgs &a, const int32_t *tokens, int64_
 hipError_t launch_append_ngram(const NgramArgs &a, const int32_t *tokens, int64_t tokens_stride,
                                const int32_t *counts, int32_t batch, hipStream_t s);
 hipError_t launch_ngram_draft(const NgramArgs &a, const NgramDraftArgs &d, hipStream_t s);
+hipError_t launch_append_draft_ngram(const NgramArgs &a, const int32_t *tokens,
+                                     int64_t tokens_stride, const int32_t *counts,
+                                     const NgramDraftArgs &d, hipStream_t s);
 hipError_t launch_ngram_clear(const NgramArgs &a, int32_t batch, hipStream_t s);
 
 }  // namespace pld

@@ -259,3 +259,127 @@ def test_ngram_rejects_lengths_beyond_cache():
             s.draft(P(min_percent=(50, 101, 50, 50)), 8)
     finally:
         s.close()
+
+
+def test_ngram_append_longer_than_stride():
+    """Source rows 8 tokens apart with counts up to 1,500 (rows overlap): the
+    one-workgroup append reads such long appends from memory instead of its
+    LDS window, and still counts exactly."""
+    import torch
+    rng = np.random.default_rng(9205)
+    batch, stride = 6, 8
+    counts = np.array([1500, 0, 1029, 1024, 7, 1100], np.int32)
+    src = rng.integers(0, 4, (batch - 1) * stride + int(counts.max())).astype(np.int32)
+    s = NgramStore(batch, 4000)
+    try:
+        s.append([rng.integers(0, 4, 30).astype(np.int32) for _ in range(batch)])
+        for b in range(batch):
+            s.host[b] = np.concatenate([s.host[b], src[b * stride:b * stride + counts[b]]])
+        B.pld_append(s.ctx, torch.from_numpy(src).cuda(), stride, torch.from_numpy(counts).cuda(),
+                     batch)
+        s.check(P(), 32, "overlapping rows")
+    finally:
+        s.close()
+
+
+def test_ngram_append_draft_streaming_workload():
+    """The streaming workload through pld_append_draft_ngram (append and
+    draft in one launch per step), checked every 4th step and at the end;
+    the appended tokens follow the lookup oracle's drafts as above."""
+    import torch
+    start = wl.config5_start()
+    s = NgramStore(start.batch, wl.STREAM_MAX_LEN)
+    lib_p = to_lib(P())
+    d = torch.empty((start.batch, start.k_max), dtype=torch.int32, device="cuda")
+    n = torch.empty(start.batch, dtype=torch.int32, device="cuda")
+    lv = torch.empty_like(d)
+    try:
+        s.append(start.histories)
+        for step in range(wl.STREAM_STEPS):
+            ld, ll, _, _ = oracle.draft(s.host, start.n_min, start.n_max, start.k_max)
+            counts, fresh = wl.stream_step_draws(step)
+            tok = wl.compose_append(ld, ll, counts, fresh)
+            for b in range(start.batch):
+                s.host[b] = np.concatenate([s.host[b], tok[b, :counts[b]]])
+            B.pld_append_draft_ngram(s.ctx, torch.from_numpy(tok).cuda(), tok.shape[1],
+                                     torch.from_numpy(counts).cuda(), start.batch, lib_p,
+                                     start.k_max, d, n, lv)
+            if step % 4 == 3 or step == wl.STREAM_STEPS - 1:
+                assert B.pld_sync(s.ctx) == B.PLD_OK
+                od, on, olv = oracle.ngram_draft(P(), s.host, start.k_max)
+                assert (d.cpu().numpy() == od).all(), f"step {step}"
+                assert (n.cpu().numpy() == on).all() and (lv.cpu().numpy() == olv).all()
+    finally:
+        s.close()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_ngram_append_draft_fuzz(seed):
+    """Random streams through pld_append_draft_ngram: tiny alphabets, counts
+    of 0..40 (some rows past capacity, so rejected), source strides of 0
+    (every row reads the same tokens), 40 (one launch) and 1,100 (append and
+    draft as two calls), random thresholds; every step checked."""
+    import torch
+    rng = np.random.default_rng([9206, seed])
+    batch = int(rng.integers(1, 9))
+    alpha = int(rng.integers(2, 5))
+    max_len = 600
+    s = NgramStore(batch, max_len)
+    try:
+        s.append([rng.integers(0, alpha, int(rng.integers(0, 500))).astype(np.int32)
+                  for _ in range(batch)])
+        for step in range(30):
+            stride = int(rng.choice([0, 40, 1100]))
+            width = max(stride, 40)
+            src = rng.integers(0, alpha, (batch, width)).astype(np.int32)
+            if stride == 0:
+                src[:] = src[0]
+            counts = rng.integers(0, 41, batch).astype(np.int32)
+            flat = src.reshape(-1) if stride else src[0]
+            status_expect = B.PLD_OK
+            for b in range(batch):
+                row = flat[b * stride:b * stride + counts[b]] if stride else flat[:counts[b]]
+                if len(s.host[b]) + counts[b] <= max_len:
+                    s.host[b] = np.concatenate([s.host[b], row])
+                else:
+                    status_expect = B.PLD_ECAPACITY
+            p = pins.random_params(rng)
+            k = int(rng.integers(1, 40))
+            d = torch.empty((batch, k), dtype=torch.int32, device="cuda")
+            n = torch.empty(batch, dtype=torch.int32, device="cuda")
+            lv = torch.empty_like(d)
+            B.pld_append_draft_ngram(s.ctx, torch.from_numpy(np.ascontiguousarray(flat)).cuda(),
+                                     stride, torch.from_numpy(counts).cuda(), batch, to_lib(p),
+                                     k, d, n, lv)
+            assert B.pld_sync(s.ctx) == status_expect, f"seed {seed} step {step}"
+            od, on, olv = oracle.ngram_draft(p, s.host, k)
+            assert (d.cpu().numpy() == od).all(), f"seed {seed} step {step} stride {stride}"
+            assert (n.cpu().numpy() == on).all() and (lv.cpu().numpy() == olv).all()
+    finally:
+        s.close()
+
+
+def test_ngram_append_draft_long_rows():
+    """Counts above the one-launch window (rows 8 tokens apart, up to 1,500
+    tokens): the fused kernel reads such appends from memory."""
+    import torch
+    rng = np.random.default_rng(9207)
+    batch, stride = 5, 8
+    counts = np.array([1500, 3, 1030, 0, 1200], np.int32)
+    src = rng.integers(0, 3, (batch - 1) * stride + int(counts.max())).astype(np.int32)
+    s = NgramStore(batch, 4000)
+    try:
+        s.append([rng.integers(0, 3, 50).astype(np.int32) for _ in range(batch)])
+        for b in range(batch):
+            s.host[b] = np.concatenate([s.host[b], src[b * stride:b * stride + counts[b]]])
+        d = torch.empty((batch, 24), dtype=torch.int32, device="cuda")
+        n = torch.empty(batch, dtype=torch.int32, device="cuda")
+        lv = torch.empty_like(d)
+        B.pld_append_draft_ngram(s.ctx, torch.from_numpy(src).cuda(), stride,
+                                 torch.from_numpy(counts).cuda(), batch, to_lib(P()), 24, d, n,
+                                 lv)
+        assert B.pld_sync(s.ctx) == B.PLD_OK
+        od, on, olv = oracle.ngram_draft(P(), s.host, 24)
+        assert (d.cpu().numpy() == od).all() and (lv.cpu().numpy() == olv).all()
+    finally:
+        s.close()
