@@ -42,16 +42,30 @@ METRIC_NGRAM = ("successor-count n-gram draft steps/s (llama.cpp context cache r
                 "batched, exact)")
 METRIC_FUSE = ("lookup draft + draft fusion and long-block scheduling steps/s "
                "(HyperQwen lookup-drafting page, steps 1-3)")
-PROFILE = os.path.join(ROOT, "profiles", "pld_scan_c4_b16x262144.md")
+# counter summaries of pld_scan per lookup workload (default launch)
+PROFILES = {1: "pld_scan_c1_b1x4096.md", 2: "pld_scan_c2_b8x25000.md",
+            3: "pld_scan_c3_b64_ragged.md", 4: "pld_scan_c4_b16x262144.md"}
 KERNEL_SRC = os.path.join(ROOT, "prompt_lookup_gram_amd", "csrc", "pld_kernels.hip")
 
 
-def profiled_traffic():
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the kernel source as it is now (else None)."""
+def calibration_copies(torch, dev):
+    """8 device copies of a 64 MiB int32 tensor: a kernel of known size whose
+    FETCH_SIZE / WRITE_SIZE scale the counter profiles."""
+    src = torch.randint(0, 1 << 30, (16 << 20,), dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(8):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def profiled_traffic(config: int = 4):
+    """HBM bytes per launch from the workload's committed counter summary,
+    if it was taken on the kernel source as it is now (else None)."""
     import hashlib
+    if config not in PROFILES:
+        return None
     try:
-        text = open(PROFILE).read()
+        text = open(os.path.join(ROOT, "profiles", PROFILES[config])).read()
         src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
     except OSError:
         return None
@@ -290,17 +304,13 @@ def main():
     B.pld_destroy(ctx)
 
     if args.calibrate_copy:
-        src = torch.randint(0, 1 << 30, (16 << 20,), dtype=torch.int32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(8):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+        calibration_copies(torch, dev)
 
     graph_us = gpu_ms * 1e3 / steps           # mean launch time (one kernel per step)
     scan_gbps = bytes_step / (graph_us * 1e-6) / 1e9
-    default_launch = (args.tile in (0, 4096) and args.fused in (-1, 1) and args.config == 4
+    default_launch = (args.tile in (0, 4096) and args.fused in (-1, 1)
                       and args.layout == "strided")
-    traffic = profiled_traffic() if default_launch else None
+    traffic = profiled_traffic(args.config) if default_launch else None
     rec = {
         "metric": METRIC,
         "value": round(steps_per_s, 1),
@@ -740,6 +750,8 @@ def bench_stream(args, torch, B, wl, dev):
             times.append((wall, e0.elapsed_time(e1) * 1e-3))
     assert B.pld_sync(ctx) == B.PLD_OK
     B.pld_destroy(ctx)
+    if args.calibrate_copy:
+        calibration_copies(torch, dev)
     wall = float(np.median([t[0] for t in times]))
     gpu_s = float(np.median([t[1] for t in times]))
     bytes_mean = 4.0 * total_tokens / steps_n
