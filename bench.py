@@ -118,6 +118,9 @@ def parse():
     ap.add_argument("--control", action="store_true",
                     help="workload 5 only: each step also runs the online cost/benefit "
                          "controller (pld_control) on the step's lookup drafts")
+    ap.add_argument("--control-fused", action="store_true",
+                    help="workload 5, scan drafting: the controller step runs in the draft's "
+                         "own launch (pld_draft_control_batch)")
     ap.add_argument("--append-draft", action="store_true",
                     help="workload 5 only: each step's append and the next step's draft "
                          "as one pld_append_draft_store call")
@@ -160,6 +163,12 @@ def main():
     dev = torch.device("cuda:0")
     B.load()
 
+    if args.control_fused:
+        args.control = True
+        if args.index or args.ngram or args.append_draft or args.config != 5:
+            print("--control-fused: workload 5 with scan drafting only (pld_draft_control_batch)",
+                  file=sys.stderr)
+            sys.exit(2)
     if args.ngram and (args.index or args.fuse != "none"):
         print("--ngram drafts from the successor-count cache: it does not combine with "
               "--index or --fuse", file=sys.stderr)
@@ -658,7 +667,7 @@ def bench_stream(args, torch, B, wl, dev):
     c_src = torch.empty(nb, dtype=torch.int32, device=dev)
 
     def control():
-        if args.control:
+        if args.control and not args.control_fused:
             B.pld_control(ctx, cparams, c_acc, c_time, out[1], out[2], c_state, nb, c_src)
 
     nparams = B.pld_ngram_params_default()
@@ -669,6 +678,10 @@ def bench_stream(args, torch, B, wl, dev):
         elif args.index:
             B.pld_draft_store(ctx, nb, start.n_min, start.n_max, start.k_max, out[0], out[1],
                               out[2])
+        elif args.control_fused:
+            B.pld_draft_control_batch(ctx, rows, lens, nb, start.n_min, start.n_max,
+                                      start.k_max, out[0], out[1], out[2], cparams, c_acc,
+                                      c_time, c_state, c_src)
         else:
             B.pld_draft_batch(ctx, rows, lens, nb, start.n_min, start.n_max, start.k_max,
                               out[0], out[1], out[2])
@@ -773,8 +786,10 @@ def bench_stream(args, torch, B, wl, dev):
                    "k_max": start.k_max, "mean_bytes_per_step": round(bytes_mean),
                    "drafting": ("successor-count cache" if args.ngram else
                                 "n-gram index" if args.index else "scan"),
-                   "calls_per_step": (1 if args.append_draft else 2) + int(args.control),
-                   "controller": bool(args.control)},
+                   "calls_per_step": ((1 if args.append_draft else 2)
+                                      + int(args.control and not args.control_fused)),
+                   "controller": ("in the draft's launch" if args.control_fused else
+                                  "own launch" if args.control else None)},
         "us_per_step_append_plus_draft": round(gpu_s * 1e6 / steps_n, 3),
         # for the index: the history bytes a scan would have read, per second
         ("scan_equivalent_GBps" if args.index else "scan_GBps"):

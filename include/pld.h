@@ -491,6 +491,23 @@ pld_status pld_append_draft_ngram(pld_ctx *ctx, const int32_t *tokens, int64_t t
                                   hipStream_t stream);
 
 /*
+ * pld_draft_batch and pld_control in one launch: the workgroup that emits a
+ * request's lookup draft also runs its controller step, with this call's
+ * draft length and match length as the step's lookup draft. Arguments as in
+ * pld_draft_batch (no out_pos) and pld_control (no lookup_len,
+ * lookup_match: they are out_len, out_match). Results are identical to the
+ * two calls in a row.
+ * Errors: those of pld_draft_batch and pld_control.
+ */
+pld_status pld_draft_control_batch(pld_ctx *ctx, const int32_t *const *histories,
+                                   const int32_t *lengths, int32_t batch, int32_t n_min,
+                                   int32_t n_max, int32_t k_max, int32_t *out_draft,
+                                   int32_t *out_len, int32_t *out_match,
+                                   const pld_control_params *params, const int32_t *accepted,
+                                   const double *round_time, double *state, int32_t *out_source,
+                                   double *out_rates, hipStream_t stream);
+
+/*
  * Wait for the stream, then report and clear the sticky device-side flag:
  * PLD_OK when clear; PLD_ECAPACITY when a history exceeded max_len (or its
  * row's stride) or an append overflowed; PLD_EINVAL when a length or count

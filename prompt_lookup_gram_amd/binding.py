@@ -34,7 +34,7 @@ EXPORTS = ("pld_create", "pld_create_indexed", "pld_destroy", "pld_configure", "
            "pld_fuse_params_default",
            "pld_fuse", "pld_draft_fuse_batch", "pld_control_params_default", "pld_control",
            "pld_ngram_params_default", "pld_create_ngram", "pld_draft_ngram",
-           "pld_append_draft_ngram",
+           "pld_append_draft_ngram", "pld_draft_control_batch",
            "pld_sync", "pld_strerror",
            "pld_last_error")
 
@@ -116,6 +116,8 @@ def load(path: str = LIB_PATH):
         "pld_draft_ngram": [vp, ctypes.POINTER(PldNgramParams), i32, i32, vp, vp, vp, vp],
         "pld_append_draft_ngram": [vp, vp, i64, vp, i32, ctypes.POINTER(PldNgramParams), i32,
                                    vp, vp, vp, vp],
+        "pld_draft_control_batch": [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp,
+                                    ctypes.POINTER(PldControlParams), vp, vp, vp, vp, vp, vp],
         "pld_sync": [vp, vp],
     }
     for name, args in sig.items():
@@ -363,6 +365,23 @@ def pld_control(ctx: int, params: PldControlParams, accepted, round_time, lookup
         ctx, ctypes.byref(params), _dev_ptr(accepted, "accepted", i32),
         _dev_ptr(round_time, "round_time", f64), _dev_ptr(lookup_len, "lookup_len", i32),
         _dev_ptr(lookup_match, "lookup_match", i32), _dev_ptr(state, "state", f64), int(batch),
+        _dev_ptr(out_source, "out_source", i32), _dev_ptr(out_rates, "out_rates", f64),
+        _stream(stream)))
+
+
+def pld_draft_control_batch(ctx: int, histories, lengths, batch: int, n_min: int, n_max: int,
+                            k_max: int, out_draft, out_len, out_match, params: PldControlParams,
+                            accepted, round_time, state, out_source, out_rates=None,
+                            stream=None) -> None:
+    """pld_draft_batch and pld_control in one launch (include/pld.h)."""
+    import torch
+    i32, f64 = _i32(), torch.float64
+    _check("pld_draft_control_batch", load().pld_draft_control_batch(
+        ctx, _dev_ptr(histories, "histories", torch.int64), _dev_ptr(lengths, "lengths", i32),
+        int(batch), int(n_min), int(n_max), int(k_max), _dev_ptr(out_draft, "out_draft", i32),
+        _dev_ptr(out_len, "out_len", i32), _dev_ptr(out_match, "out_match", i32),
+        ctypes.byref(params), _dev_ptr(accepted, "accepted", i32),
+        _dev_ptr(round_time, "round_time", f64), _dev_ptr(state, "state", f64),
         _dev_ptr(out_source, "out_source", i32), _dev_ptr(out_rates, "out_rates", f64),
         _stream(stream)))
 

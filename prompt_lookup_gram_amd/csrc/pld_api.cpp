@@ -111,7 +111,8 @@ pld_status draft(pld_ctx *ctx, const int32_t *const *histories, const int32_t *b
                  int64_t stride, int32_t min_len, const int32_t *lengths,
                  int32_t batch, int32_t n_min, int32_t n_max, int32_t k_max,
                  int32_t *out_draft, int32_t *out_len, int32_t *out_match,
-                 int32_t *out_pos, hipStream_t stream, const pld::FuseArgs *fuse = nullptr)
+                 int32_t *out_pos, hipStream_t stream, const pld::FuseArgs *fuse = nullptr,
+                 const pld::ControlArgs *control = nullptr)
 {
     // a strided batch stands in for the row table in the common checks
     const int32_t *const *rows_or_base =
@@ -156,6 +157,11 @@ pld_status draft(pld_ctx *ctx, const int32_t *const *histories, const int32_t *b
         a.fuse = *fuse;
     else
         memset(&a.fuse, 0, sizeof(a.fuse));
+    a.do_control = control != nullptr;
+    if (control)
+        a.control = *control;
+    else
+        memset(&a.control, 0, sizeof(a.control));
     hipError_t e = pld::launch_draft(a, ctx->tile_tokens, stream);
     if (e != hipSuccess)
         return hip_fail(e, "draft kernel launch");
@@ -368,6 +374,58 @@ pld_status create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t own
     *out = c;
     return PLD_OK;
 }
+
+// Checks a controller step's arguments and fills `a`; PLD_OK or the
+// failure. With `own_lookup` the lookup draft comes from the same call (no
+// lookup_len / lookup_match buffers).
+pld_status control_args(pld_ctx *ctx, const pld_control_params *params, const int32_t *accepted,
+                        const double *round_time, const int32_t *lookup_len,
+                        const int32_t *lookup_match, double *state, int32_t batch,
+                        int32_t *out_source, double *out_rates, bool own_lookup,
+                        pld::ControlArgs &a)
+{
+    if (!ctx)
+        return fail(PLD_EINVAL, "ctx is null");
+    if (!params)
+        return fail(PLD_EINVAL, "params is null");
+    const pld_control_params &p = *params;
+    if (!(p.alpha >= 0.0 && p.alpha <= 1.0 && p.beta >= 0.0 && p.beta <= 1.0))
+        return fail(PLD_EINVAL, "alpha and beta must be in [0, 1]");
+    if (!(p.margin > 0.0) || !(p.prior_accept >= 0.0 && p.prior_accept <= 1.0) ||
+        !(p.prior_time > 0.0))
+        return fail(PLD_EINVAL, "need margin > 0, prior_accept in [0, 1], prior_time > 0");
+    if (p.mtp_tokens < 0 || p.bucket_edge[0] > p.bucket_edge[1] ||
+        p.bucket_edge[1] > p.bucket_edge[2])
+        return fail(PLD_EINVAL, "need mtp_tokens >= 0 and nondecreasing bucket edges");
+    if (batch < 0 || batch > ctx->max_batch)
+        return fail(PLD_EINVAL, "batch %d outside [0, max_batch=%d]", batch, ctx->max_batch);
+    if (batch > 0 && (!accepted || !round_time || !state || !out_source ||
+                      (!own_lookup && (!lookup_len || !lookup_match))))
+        return fail(PLD_EINVAL, "null buffer pointer");
+    if ((((uintptr_t)accepted | (uintptr_t)lookup_len | (uintptr_t)lookup_match |
+          (uintptr_t)out_source) & 3u) ||
+        (((uintptr_t)round_time | (uintptr_t)state | (uintptr_t)out_rates) & 7u))
+        return fail(PLD_EINVAL, "misaligned buffer (int32: 4 bytes, double: 8 bytes)");
+    a.alpha = p.alpha;
+    a.beta = p.beta;
+    a.margin = p.margin;
+    a.prior_accept = p.prior_accept;
+    a.prior_time = p.prior_time;
+    a.mtp_tokens = p.mtp_tokens;
+    for (int i = 0; i < 3; ++i)
+        a.edge[i] = p.bucket_edge[i];
+    a.accepted = accepted;
+    a.round_time = round_time;
+    a.lookup_len = lookup_len;
+    a.lookup_match = lookup_match;
+    a.state = state;
+    a.batch = batch;
+    a.out_source = out_source;
+    a.out_rates = out_rates;
+    a.err = ctx->err;
+    return PLD_OK;
+}
+
 
 }  // namespace
 
@@ -789,56 +847,39 @@ pld_status pld_control_params_default(pld_control_params *params)
     return PLD_OK;
 }
 
+
 pld_status pld_control(pld_ctx *ctx, const pld_control_params *params, const int32_t *accepted,
                        const double *round_time, const int32_t *lookup_len,
                        const int32_t *lookup_match, double *state, int32_t batch,
                        int32_t *out_source, double *out_rates, hipStream_t stream)
 {
-    if (!ctx)
-        return fail(PLD_EINVAL, "ctx is null");
-    if (!params)
-        return fail(PLD_EINVAL, "params is null");
-    const pld_control_params &p = *params;
-    if (!(p.alpha >= 0.0 && p.alpha <= 1.0 && p.beta >= 0.0 && p.beta <= 1.0))
-        return fail(PLD_EINVAL, "alpha and beta must be in [0, 1]");
-    if (!(p.margin > 0.0) || !(p.prior_accept >= 0.0 && p.prior_accept <= 1.0) ||
-        !(p.prior_time > 0.0))
-        return fail(PLD_EINVAL, "need margin > 0, prior_accept in [0, 1], prior_time > 0");
-    if (p.mtp_tokens < 0 || p.bucket_edge[0] > p.bucket_edge[1] ||
-        p.bucket_edge[1] > p.bucket_edge[2])
-        return fail(PLD_EINVAL, "need mtp_tokens >= 0 and nondecreasing bucket edges");
-    if (batch < 0 || batch > ctx->max_batch)
-        return fail(PLD_EINVAL, "batch %d outside [0, max_batch=%d]", batch, ctx->max_batch);
-    if (batch == 0)
-        return PLD_OK;
-    if (!accepted || !round_time || !lookup_len || !lookup_match || !state || !out_source)
-        return fail(PLD_EINVAL, "null buffer pointer");
-    if ((((uintptr_t)accepted | (uintptr_t)lookup_len | (uintptr_t)lookup_match |
-          (uintptr_t)out_source) & 3u) ||
-        (((uintptr_t)round_time | (uintptr_t)state | (uintptr_t)out_rates) & 7u))
-        return fail(PLD_EINVAL, "misaligned buffer (int32: 4 bytes, double: 8 bytes)");
     pld::ControlArgs a;
-    a.alpha = p.alpha;
-    a.beta = p.beta;
-    a.margin = p.margin;
-    a.prior_accept = p.prior_accept;
-    a.prior_time = p.prior_time;
-    a.mtp_tokens = p.mtp_tokens;
-    for (int i = 0; i < 3; ++i)
-        a.edge[i] = p.bucket_edge[i];
-    a.accepted = accepted;
-    a.round_time = round_time;
-    a.lookup_len = lookup_len;
-    a.lookup_match = lookup_match;
-    a.state = state;
-    a.batch = batch;
-    a.out_source = out_source;
-    a.out_rates = out_rates;
-    a.err = ctx->err;
+    pld_status st = control_args(ctx, params, accepted, round_time, lookup_len, lookup_match,
+                                 state, batch, out_source, out_rates, false, a);
+    if (st != PLD_OK || batch == 0)
+        return st;
     hipError_t e = pld::launch_control(a, stream);
     if (e != hipSuccess)
         return hip_fail(e, "control kernel launch");
     return PLD_OK;
+}
+
+pld_status pld_draft_control_batch(pld_ctx *ctx, const int32_t *const *histories,
+                                   const int32_t *lengths, int32_t batch, int32_t n_min,
+                                   int32_t n_max, int32_t k_max, int32_t *out_draft,
+                                   int32_t *out_len, int32_t *out_match,
+                                   const pld_control_params *params, const int32_t *accepted,
+                                   const double *round_time, double *state, int32_t *out_source,
+                                   double *out_rates, hipStream_t stream)
+{
+    // the lookup draft the controller reads is this call's own output
+    pld::ControlArgs c;
+    pld_status st = control_args(ctx, params, accepted, round_time, out_len, out_match, state,
+                                 batch, out_source, out_rates, true, c);
+    if (st != PLD_OK)
+        return st;
+    return draft(ctx, histories, nullptr, 0, 0, lengths, batch, n_min, n_max, k_max, out_draft,
+                 out_len, out_match, nullptr, stream, nullptr, &c);
 }
 
 pld_status pld_sync(pld_ctx *ctx, hipStream_t stream)

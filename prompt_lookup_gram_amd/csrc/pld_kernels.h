@@ -51,6 +51,22 @@ struct FuseArgs {
     unsigned int *err;
 };
 
+// The online cost/benefit controller (pld_control.hip, pld_control_step.h).
+struct ControlArgs {
+    double alpha, beta, margin, prior_accept, prior_time;
+    int32_t mtp_tokens;
+    int32_t edge[3];
+    const int32_t *accepted;      // [batch]
+    const double *round_time;     // [batch]
+    const int32_t *lookup_len;    // [batch]
+    const int32_t *lookup_match;  // [batch]
+    double *state;                // [batch * 11]
+    int32_t batch;
+    int32_t *out_source;          // [batch]
+    double *out_rates;            // [batch * 3] or null
+    unsigned int *err;
+};
+
 struct DraftArgs {
     const int32_t *const *histories;  // row table (stride == 0)
     const int32_t *base;              // strided batch: row b at base + b * stride
@@ -70,6 +86,8 @@ struct DraftArgs {
     const int4 *zero16;            // 16 zero bytes (edge-chunk load target)
     FuseArgs fuse;                 // the fusion step, when do_fuse
     int32_t do_fuse;               // emit also fuses (pld_draft_fuse_batch)
+    ControlArgs control;           // the controller step, when do_control
+    int32_t do_control;            // emit also runs it (pld_draft_control_batch)
 };
 
 struct AppendArgs {
@@ -126,21 +144,6 @@ struct NgramDraftArgs {
     int32_t *out_levels;  // [batch, k_max] or null
 };
 
-// The online cost/benefit controller (pld_control.hip).
-struct ControlArgs {
-    double alpha, beta, margin, prior_accept, prior_time;
-    int32_t mtp_tokens;
-    int32_t edge[3];
-    const int32_t *accepted;      // [batch]
-    const double *round_time;     // [batch]
-    const int32_t *lookup_len;    // [batch]
-    const int32_t *lookup_match;  // [batch]
-    double *state;                // [batch * 11]
-    int32_t batch;
-    int32_t *out_source;          // [batch]
-    double *out_rates;            // [batch * 3] or null
-    unsigned int *err;
-};
 
 // Workgroups the scan launches for a batch (tiles per request x batch).
 int64_t scan_grid(int32_t max_len, int32_t batch, int tile_tokens);

@@ -46,6 +46,7 @@
 
 #include <type_traits>
 
+#include "pld_control_step.h"
 #include "pld_kernels.h"
 
 namespace pld {
@@ -298,17 +299,76 @@ __device__ __forceinline__ void emit_and_fuse(const DraftArgs &a, int b, const R
     fuse_request(a.fuse, b, lane, d, m, lk, pre);
 }
 
+// The inputs of a request's controller step that do not depend on its
+// lookup draft, one value per lane of a wavefront: lane i < 11 holds state
+// word i, every lane the round time and accepted count of the previous
+// round. Every lane loads (indices clamped), so no load sits in a branch.
+struct CtlPre {
+    double sv, rt;
+    int32_t acc;
+};
+
+__device__ __forceinline__ CtlPre control_preload(const ControlArgs &a, int b, int lane)
+{
+    CtlPre p;
+    p.sv = a.state[(int64_t)b * kCtlWords + (lane < kCtlWords ? lane : kCtlWords - 1)];
+    p.rt = a.round_time[b];
+    p.acc = a.accepted[b];
+    return p;
+}
+
+// The controller step of request b from its lookup draft (d tokens, match
+// m), by one wavefront holding its preloaded inputs; lane 0 writes.
+__device__ __forceinline__ void emit_control(const ControlArgs &a, int b, int32_t d, int32_t m,
+                                             int lane, const CtlPre &pre)
+{
+    auto word = [&](int i) {
+        const u64 w = (u64)__double_as_longlong(pre.sv);
+        const u64 lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)w, i);
+        const u64 hi = (uint32_t)__builtin_amdgcn_readlane((int)(w >> 32), i);
+        return __longlong_as_double((long long)(hi << 32 | lo));
+    };
+    CtlState st;
+    st.acc = ctl_double4{word(kCtlAcc0), word(kCtlAcc0 + 1), word(kCtlAcc0 + 2),
+                         word(kCtlAcc0 + 3)};
+    st.acc_mtp = word(kCtlAccMtp);
+    st.t_plain = word(kCtlTPlain);
+    st.t_mtp = word(kCtlTMtp);
+    st.t_lookup = word(kCtlTLookup);
+    st.last_src = word(kCtlLastSrc);
+    st.last_bucket = word(kCtlLastBucket);
+    st.last_drafted = word(kCtlLastDrafted);
+    const ControlResult res = control_step(a, st, pre.acc, pre.rt, d, m);
+    if (lane == 0) {
+        ctl_store(a.state + (int64_t)b * kCtlWords, st);
+        control_write(a, b, res);
+    }
+}
+
 // The emit step of a request by the workgroup that holds its final key:
-// lookup outputs only, or lookup outputs and fusion (wavefront 0).
-template <bool FUSE>
+// lookup outputs only, or lookup outputs and fusion (wavefront 0), or
+// lookup outputs and the controller step (wavefront 0).
+template <bool FUSE, bool CONTROL>
 __device__ __forceinline__ void emit_request(const DraftArgs &a, int b, const Req &r, u64 key,
-                                             int tid, int nthreads, const FusePre &pre)
+                                             int tid, int nthreads, const FusePre &pre,
+                                             const CtlPre &cpre)
 {
     if constexpr (FUSE) {
         if (tid < kWave)
             emit_and_fuse(a, b, r, key, tid, pre);
     } else {
         emit(a, b, r, key, tid, nthreads);
+        if constexpr (CONTROL) {
+            if (tid < kWave) {
+                int32_t m = 0, d = 0;
+                if (key != 0) {
+                    m = (int32_t)(key >> 32);
+                    const int32_t follow = r.L - 1 - (int32_t)(key & 0xffffffffu);
+                    d = follow < a.k_max ? follow : a.k_max;
+                }
+                emit_control(a.control, b, d, m, tid, cpre);
+            }
+        }
     }
 }
 
@@ -568,7 +628,7 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
 // caller's bound min_len (checked against each length on the device) then
 // issues its loads at once, before its length is read from memory; other
 // tiles, and row-table batches, read the length and row first.
-template <int TILE, int THREADS, bool STRIDED, bool FUSE>
+template <int TILE, int THREADS, bool STRIDED, bool FUSE, bool CONTROL>
 __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int32_t *lengths,
                                                     int32_t batch, int32_t max_len,
                                                     int32_t n_min, int32_t n_max, int64_t stride,
@@ -619,6 +679,9 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
     FusePre pre{};
     if constexpr (FUSE)
         pre = fuse_preload(a.fuse, b, tid & (kWave - 1));
+    CtlPre cpre{};
+    if constexpr (CONTROL)
+        cpre = control_preload(a.control, b, tid & (kWave - 1));
     if (tile >= r.ntiles)
         return;  // this request has no candidates in this tile
     if (r.err && tid == 0)
@@ -689,7 +752,7 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
     }
     __syncthreads();
     if (s_last)
-        emit_request<FUSE>(a, b, r, wg_best, tid, THREADS, pre);
+        emit_request<FUSE, CONTROL>(a, b, r, wg_best, tid, THREADS, pre, cpre);
 }
 
 __global__ __launch_bounds__(kWave) void pld_gather(DraftArgs a)
@@ -698,10 +761,14 @@ __global__ __launch_bounds__(kWave) void pld_gather(DraftArgs a)
     const Req r = load_req(a, b, 1);
     const u64 key = a.slots[b].key;
     if (a.do_fuse)
-        emit_request<true>(a, b, r, r.err ? 0ull : key, threadIdx.x, kWave,
-                           fuse_preload(a.fuse, b, threadIdx.x));
+        emit_request<true, false>(a, b, r, r.err ? 0ull : key, threadIdx.x, kWave,
+                                  fuse_preload(a.fuse, b, threadIdx.x), CtlPre{});
+    else if (a.do_control)
+        emit_request<false, true>(a, b, r, r.err ? 0ull : key, threadIdx.x, kWave, FusePre{},
+                                  control_preload(a.control, b, threadIdx.x));
     else
-        emit_request<false>(a, b, r, r.err ? 0ull : key, threadIdx.x, kWave, FusePre{});
+        emit_request<false, false>(a, b, r, r.err ? 0ull : key, threadIdx.x, kWave, FusePre{},
+                                   CtlPre{});
     __syncthreads();
     if (threadIdx.x == 0 && key != 0)
         a.slots[b].key = 0;
@@ -765,18 +832,24 @@ template <int TILE, int THREADS>
 hipError_t launch_scan(const DraftArgs &a, int64_t tiles_per_req, hipStream_t s)
 {
     const int64_t grid = tiles_per_req * a.batch;
-    if (a.stride && a.do_fuse)
+    if (a.stride && (a.do_fuse || a.do_control))
         return hipErrorInvalidValue;  // no entry point fuses a strided batch
+    if (a.do_fuse && a.do_control)
+        return hipErrorInvalidValue;  // no entry point does both
     if (a.stride)
-        hipLaunchKernelGGL((pld_scan<TILE, THREADS, true, false>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((pld_scan<TILE, THREADS, true, false, false>), dim3((unsigned)grid),
                            dim3(THREADS), 0, s, (const void *)a.base, a.lengths, a.batch,
                            a.max_len, a.n_min, a.n_max, a.stride, a.min_len, a);
     else if (a.do_fuse && a.fused)
-        hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, true>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, true, false>), dim3((unsigned)grid),
+                           dim3(THREADS), 0, s, (const void *)a.histories, a.lengths, a.batch,
+                           a.max_len, a.n_min, a.n_max, (int64_t)0, 0, a);
+    else if (a.do_control && a.fused)
+        hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, false, true>), dim3((unsigned)grid),
                            dim3(THREADS), 0, s, (const void *)a.histories, a.lengths, a.batch,
                            a.max_len, a.n_min, a.n_max, (int64_t)0, 0, a);
     else
-        hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, false>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, false, false>), dim3((unsigned)grid),
                            dim3(THREADS), 0, s, (const void *)a.histories, a.lengths, a.batch,
                            a.max_len, a.n_min, a.n_max, (int64_t)0, 0, a);
     return hipGetLastError();

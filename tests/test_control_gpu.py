@@ -158,3 +158,70 @@ def test_control_bad_outcomes_flagged():
                           d, m, state, 3, src)
     finally:
         B.pld_destroy(ctx)
+
+
+@pytest.mark.parametrize("fused_gather", [1, 0])
+def test_draft_control_batch_matches_oracles(fused_gather):
+    """pld_draft_control_batch (the lookup draft and the controller step in
+    one launch; with fused_gather 0 the gather kernel runs the step): every
+    step drafts prefixes of random length of the ragged workload's 64
+    histories, so drafts and match lengths change from step to step; the
+    draft must equal the lookup oracle's and the controller's state, rates
+    and choices the controller oracle's fed with those drafts."""
+    import torch
+    from prompt_lookup_gram_amd import workloads as wl
+    w = wl.config3()
+    batch = w.batch
+    db = B.DeviceBatch(w.histories)
+    ctx = B.pld_create(batch, db.max_len)
+    B.pld_configure(ctx, 0, fused_gather)
+    op, gp = both_params(margin=1.02)
+    rng = np.random.default_rng([7302, fused_gather])
+    state = torch.zeros((batch, W), dtype=torch.float64, device="cuda")
+    ostate = np.zeros((batch, W))
+    drafted = np.zeros(batch, np.int64)
+    seen = set()
+    try:
+        for t in range(40):
+            lens = np.array([int(rng.integers(1, len(h) + 1)) for h in w.histories], np.int32)
+            acc = np.array([rng.integers(0, k + 1) for k in drafted], np.int32)
+            tm = rng.uniform(0.3, 2.0, batch)
+            out = B.alloc_outputs(batch, w.k_max)
+            src = torch.full((batch,), -7, dtype=torch.int32, device="cuda")
+            rates = torch.full((batch, 3), -7.0, dtype=torch.float64, device="cuda")
+            B.pld_draft_control_batch(ctx, db.rows, dev(lens, torch.int32), batch, w.n_min,
+                                      w.n_max, w.k_max, out[0], out[1], out[2], gp,
+                                      dev(acc, torch.int32), dev(tm, torch.float64), state, src,
+                                      rates)
+            assert B.pld_sync(ctx) == B.PLD_OK
+            prefixes = [h[:n] for h, n in zip(w.histories, lens)]
+            od, ol, om, _ = oracle.draft(prefixes, w.n_min, w.n_max, w.k_max)
+            assert np.array_equal(out[0].cpu().numpy(), od), f"step {t}: draft"
+            assert np.array_equal(out[1].cpu().numpy(), ol) and np.array_equal(
+                out[2].cpu().numpy(), om)
+            osrc, orates, ostate = oracle.control(op, acc, tm, ol, om, ostate)
+            assert np.array_equal(src.cpu().numpy(), osrc), f"step {t}: source"
+            assert np.array_equal(rates.cpu().numpy(), orates), f"step {t}: rates"
+            assert np.array_equal(state.cpu().numpy(), ostate), f"step {t}: state"
+            drafted = ostate[:, 10].astype(np.int64)
+            seen |= set(osrc.tolist())
+    finally:
+        B.pld_destroy(ctx)
+    assert len(seen) >= 2  # the trace reaches more than one source
+
+
+def test_draft_control_batch_rejects_bad_arguments():
+    import torch
+    ctx = B.pld_create(4, 64)
+    try:
+        gp = B.pld_control_params_default()
+        gp.alpha = 2.0
+        out = B.alloc_outputs(4, 8)
+        z = torch.zeros(4, dtype=torch.int32, device="cuda")
+        with pytest.raises(B.PldError):
+            B.pld_draft_control_batch(ctx, torch.zeros(4, dtype=torch.int64, device="cuda"), z,
+                                      4, 4, 12, 8, out[0], out[1], out[2], gp, z,
+                                      torch.ones(4, dtype=torch.float64, device="cuda"),
+                                      torch.zeros((4, W), dtype=torch.float64, device="cuda"), z)
+    finally:
+        B.pld_destroy(ctx)
