@@ -126,7 +126,9 @@ pld_status pld_configure(pld_ctx *ctx, int32_t tile_tokens, int32_t fused_gather
  *  counts: device int32[batch], each 0 <= counts[b].
  * A row whose append would pass max_len, or whose count is negative, is left
  * unchanged and sets the sticky flag (PLD_ECAPACITY / PLD_EINVAL at
- * pld_sync). batch == 0 is a no-op. With an index (pld_create_indexed) the
+ * pld_sync); so is a row whose stored length is outside [0, max_len] (the
+ * length array is reachable through pld_store_views), as PLD_ECAPACITY.
+ * batch == 0 is a no-op. With an index (pld_create_indexed) the
  * n-grams that the append makes draftable are inserted first, in a second
  * kernel on the same stream. With a successor-count cache
  * (pld_create_ngram) the appended tokens' n-grams are counted in the same
@@ -241,11 +243,15 @@ pld_status pld_draft_store(pld_ctx *ctx, int32_t batch, int32_t n_min, int32_t n
  * new histories (n_min, n_max, k_max and outputs as in pld_draft_store or,
  * without an index, pld_draft_batch_pos on pld_store_views; out_pos may be
  * NULL). On an indexed context n_min, n_max must lie inside the indexed
- * lengths; with 0 < tokens_stride <= 1024 both steps then run in one launch
- * (one workgroup per request), otherwise as two calls. Results are the same
- * either way. A rejected append (see pld_append) leaves its row as it was,
- * and that row is drafted as it stands. All arguments are checked before
- * anything is enqueued.
+ * lengths. With 0 < tokens_stride <= 1024 both steps run in one launch:
+ * on an indexed context one workgroup per request; on a context with a
+ * plain store (no index, no successor-count cache) and the fused gather
+ * (the default of pld_configure), inside the scan's own launch, which reads
+ * the appended positions from `tokens`. Otherwise they run as two calls.
+ * Results, the store and the reported errors are the same either way. A
+ * rejected append (see pld_append) leaves its row as it was, and that row is
+ * drafted as it stands. All arguments are checked before anything is
+ * enqueued.
  * Errors: those of pld_append and of the draft call.
  */
 pld_status pld_append_draft_store(pld_ctx *ctx, const int32_t *tokens, int64_t tokens_stride,

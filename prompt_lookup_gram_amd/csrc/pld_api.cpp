@@ -107,12 +107,19 @@ pld_status check_draft_args(pld_ctx *ctx, const int32_t *const *histories,
     return PLD_OK;
 }
 
+// An append to the context's store made inside the draft's own launch.
+struct AppendIn {
+    const int32_t *tokens;
+    int64_t tokens_stride;
+    const int32_t *counts;
+};
+
 pld_status draft(pld_ctx *ctx, const int32_t *const *histories, const int32_t *base,
                  int64_t stride, int32_t min_len, const int32_t *lengths,
                  int32_t batch, int32_t n_min, int32_t n_max, int32_t k_max,
                  int32_t *out_draft, int32_t *out_len, int32_t *out_match,
                  int32_t *out_pos, hipStream_t stream, const pld::FuseArgs *fuse = nullptr,
-                 const pld::ControlArgs *control = nullptr)
+                 const pld::ControlArgs *control = nullptr, const AppendIn *append = nullptr)
 {
     // a strided batch stands in for the row table in the common checks
     const int32_t *const *rows_or_base =
@@ -162,6 +169,12 @@ pld_status draft(pld_ctx *ctx, const int32_t *const *histories, const int32_t *b
         a.control = *control;
     else
         memset(&a.control, 0, sizeof(a.control));
+    a.do_append = append != nullptr;
+    a.app_tokens = append ? append->tokens : nullptr;
+    a.app_stride = append ? append->tokens_stride : 0;
+    a.app_counts = append ? append->counts : nullptr;
+    a.app_store = append ? ctx->store : nullptr;
+    a.app_lengths = append ? ctx->store_len : nullptr;
     hipError_t e = pld::launch_draft(a, ctx->tile_tokens, stream);
     if (e != hipSuccess)
         return hip_fail(e, "draft kernel launch");
@@ -583,7 +596,11 @@ pld_status pld_append_draft_store(pld_ctx *ctx, const int32_t *tokens, int64_t t
         return fail(PLD_EINVAL, "batch %d outside [0, max_batch=%d]", batch, ctx->max_batch);
     if (batch > 0 && (!out_draft || !out_len || !out_match))
         return fail(PLD_EINVAL, "null buffer pointer");
-    const bool fused = ctx->index && tokens_stride > 0 && tokens_stride <= kSmallAppend;
+    const bool small = tokens_stride > 0 && tokens_stride <= kSmallAppend;
+    // a store with neither an index nor a successor-count cache is drafted
+    // by scanning it; with the fused gather the append runs inside that scan
+    const bool fused_scan = !ctx->index && !ctx->ngram_grams && ctx->fused && small;
+    const bool fused = (ctx->index && small) || fused_scan;
     if (!fused) {
         // the same two steps, one after the other on the stream
         pld_status st = pld_append(ctx, tokens, tokens_stride, counts, batch, stream);
@@ -602,6 +619,12 @@ pld_status pld_append_draft_store(pld_ctx *ctx, const int32_t *tokens, int64_t t
     if (((uintptr_t)tokens | (uintptr_t)counts | (uintptr_t)out_draft | (uintptr_t)out_len |
          (uintptr_t)out_match | (uintptr_t)out_pos) & 3u)
         return fail(PLD_EINVAL, "buffers must be 4-byte aligned");
+    if (fused_scan) {
+        const AppendIn app{tokens, tokens_stride, counts};
+        return draft(ctx, nullptr, ctx->store, ctx->pitch, 0, ctx->store_len, batch, n_min,
+                     n_max, k_max, out_draft, out_len, out_match, out_pos, stream, nullptr,
+                     nullptr, &app);
+    }
     hipError_t e = pld::launch_append_draft_indexed(index_args(ctx), tokens, tokens_stride, counts,
                                                     batch, n_min, n_max, k_max, out_draft,
                                                     out_len, out_match, out_pos, stream);

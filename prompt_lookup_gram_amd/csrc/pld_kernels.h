@@ -88,6 +88,16 @@ struct DraftArgs {
     int32_t do_fuse;               // emit also fuses (pld_draft_fuse_batch)
     ControlArgs control;           // the controller step, when do_control
     int32_t do_control;            // emit also runs it (pld_draft_control_batch)
+    // An append to the context's store in the same launch, when do_append
+    // (strided batch over the store, lengths = the store's): row b gains
+    // app_counts[b] tokens from app_tokens + b * app_stride before it is
+    // drafted, as pld_append followed by the draft would leave it.
+    const int32_t *app_tokens;
+    int64_t app_stride;
+    const int32_t *app_counts;
+    int32_t *app_store;            // the store (base), written at the appended positions
+    int32_t *app_lengths;          // the store's lengths, written back
+    int32_t do_append;
 };
 
 struct AppendArgs {

@@ -120,19 +120,45 @@ __device__ __forceinline__ int32_t comp(const int4 &v, int i)
 // Per-request facts every kernel derives the same way from lengths/rows.
 struct Req {
     const int32_t *h;
+    const int32_t *src; // appended tokens: position p >= split is src[p - split]
     int32_t L;      // usable length (0 when the request is invalid)
+    int32_t split;  // positions below it are read from h (L without an append)
+    int32_t add;    // tokens appended in this launch (0 without an append)
+    uint32_t app_err; // error bits of a rejected append (0 without an append)
     int32_t ncand;  // candidate end positions: L - 1 (or 0)
     int32_t ntiles; // tiles that hold candidates (at least 1)
     uint32_t err;   // error bits for this request
 };
 
+// The error bits of appending c tokens to a row of length len (0 when the
+// append is accepted); pld_append_kernel and the appending scan agree.
+__device__ __forceinline__ uint32_t append_error(int32_t len, int32_t c, int32_t max_len)
+{
+    if (c < 0)
+        return kErrAppendNegative;
+    if (len < 0 || (int64_t)len + c > max_len)
+        return kErrAppendCapacity;
+    return 0;
+}
+
 // Row b is histories[b], or base + b * stride for a strided batch (a.stride
-// > 0, rows 16-byte aligned as checked on the host).
+// > 0, rows 16-byte aligned as checked on the host). With APPEND the row
+// first gains the counts[b] new tokens when that append is accepted.
+template <bool APPEND = false>
 __device__ __forceinline__ Req load_req(const DraftArgs &a, int b, int tile_tokens)
 {
     Req r;
-    const int32_t len = a.lengths[b];
+    const int32_t old_len = a.lengths[b];
     const int32_t *h = a.stride ? a.base + (int64_t)b * a.stride : a.histories[b];
+    r.add = 0;
+    r.app_err = 0;
+    if constexpr (APPEND) {
+        const int32_t c = a.app_counts[b];
+        r.app_err = append_error(old_len, c, a.max_len);
+        r.add = r.app_err == 0 ? c : 0;
+        r.src = a.app_tokens + (int64_t)b * a.app_stride;
+    }
+    const int32_t len = old_len + r.add;
     r.err = 0;
     if (len < 0)
         r.err |= kErrLenNegative;
@@ -144,13 +170,33 @@ __device__ __forceinline__ Req load_req(const DraftArgs &a, int b, int tile_toke
         r.err |= kErrBadRow;
     r.h = h;
     r.L = r.err ? 0 : len;
+    if constexpr (APPEND) {
+        // an accepted append leaves a valid length, so r.err is 0 whenever r.add > 0
+        r.split = r.err ? 0 : old_len;
+    } else {
+        r.split = r.L;
+        r.src = h;
+    }
     r.ncand = r.L > 0 ? r.L - 1 : 0;
     r.ntiles = r.ncand > 0 ? (int32_t)((r.ncand + (int64_t)tile_tokens - 1) / tile_tokens) : 1;
     return r;
 }
 
+// Token p of request r's history: from its row, or with APPEND from the
+// source of this launch's append when p is at or past the old length (one
+// load either way).
+template <bool APPEND>
+__device__ __forceinline__ int32_t tok_at(const Req &r, int64_t p)
+{
+    if constexpr (APPEND)
+        return gld(p < r.split ? r.h + p : r.src + (p - r.split));
+    else
+        return gld(r.h + p);
+}
+
 // Writes row b of the outputs from a packed key (0 = no match). Called by
 // all threads of a workgroup (threads stride over the k_max slots).
+template <bool APPEND = false>
 __device__ __forceinline__ void emit(const DraftArgs &a, int b, const Req &r,
                                      u64 key, int tid, int nthreads)
 {
@@ -163,8 +209,12 @@ __device__ __forceinline__ void emit(const DraftArgs &a, int b, const Req &r,
     }
     int32_t *row = a.out_draft + (int64_t)b * a.k_max;
     const int32_t *src = r.h + (int64_t)e + 1;
-    for (int t = tid; t < a.k_max; t += nthreads)
-        row[t] = t < d ? gld(src + t) : -1;
+    for (int t = tid; t < a.k_max; t += nthreads) {
+        if constexpr (APPEND)
+            row[t] = t < d ? tok_at<true>(r, (int64_t)e + 1 + t) : -1;
+        else
+            row[t] = t < d ? gld(src + t) : -1;
+    }
     if (tid == 0) {
         a.out_len[b] = d;
         a.out_match[b] = m;
@@ -384,12 +434,25 @@ __device__ __forceinline__ bool chunk_inside(int64_t p0, int32_t L)
     return p0 >= 0 && p0 + 3 < (int64_t)L;
 }
 
-__device__ __forceinline__ int4 patch_chunk(int4 v, int64_t p0, const int32_t *h, int32_t L)
+// With APPEND a chunk is loaded whole only below the old length (the row
+// holds nothing newer yet), and the appended positions are patched in from
+// the append's source.
+template <bool APPEND>
+__device__ __forceinline__ int4 patch_chunk(int4 v, int64_t p0, const Req &r)
 {
-    if (p0 + 0 >= 0 && p0 + 0 < L) v.x = gld(h + p0 + 0);
-    if (p0 + 1 >= 0 && p0 + 1 < L) v.y = gld(h + p0 + 1);
-    if (p0 + 2 >= 0 && p0 + 2 < L) v.z = gld(h + p0 + 2);
-    if (p0 + 3 >= 0 && p0 + 3 < L) v.w = gld(h + p0 + 3);
+    const int32_t L = r.L;
+    if constexpr (APPEND) {
+        if (p0 + 0 >= 0 && p0 + 0 < L) v.x = tok_at<true>(r, p0 + 0);
+        if (p0 + 1 >= 0 && p0 + 1 < L) v.y = tok_at<true>(r, p0 + 1);
+        if (p0 + 2 >= 0 && p0 + 2 < L) v.z = tok_at<true>(r, p0 + 2);
+        if (p0 + 3 >= 0 && p0 + 3 < L) v.w = tok_at<true>(r, p0 + 3);
+    } else {
+        const int32_t *h = r.h;
+        if (p0 + 0 >= 0 && p0 + 0 < L) v.x = gld(h + p0 + 0);
+        if (p0 + 1 >= 0 && p0 + 1 < L) v.y = gld(h + p0 + 1);
+        if (p0 + 2 >= 0 && p0 + 2 < L) v.z = gld(h + p0 + 2);
+        if (p0 + 3 >= 0 && p0 + 3 < L) v.w = gld(h + p0 + 3);
+    }
     return v;
 }
 
@@ -450,7 +513,7 @@ __device__ __forceinline__ void load_interior(const int4 *arow, int64_t t0, bool
         v[k] = gld_stream(real ? arow + (gq0 + kHaloChunks + k * kWave + lane) : zero16);
 }
 
-template <int TILE, int THREADS, bool CHECKED, bool FILTER3, bool PRELOADED>
+template <int TILE, int THREADS, bool CHECKED, bool FILTER3, bool PRELOADED, bool APPEND>
 __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64_t t0,
                                          int32_t mhat, int4 *lds_win, int32_t *lds_pat,
                                          int4 (&v)[WaveGeom<TILE, THREADS>::kPer + 1])
@@ -484,10 +547,18 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
     // inside a branch makes the compiler wait for it at the join). Lanes
     // without an extra chunk re-read their first chunk; lanes past the
     // suffix length re-read its first token.
-    const int32_t p1 = gld(r.h + r.L - 1);
-    const int32_t p2 = gld(r.h + r.L - 2);  // L >= 2 whenever a tile is scanned
-    const int32_t p3 = gld(r.h + r.L - (mhat >= 3 ? 3 : 1));
-    const int32_t pv = gld(r.h + r.L - mhat + (lane < mhat ? lane : 0));
+    int32_t p1, p2, p3, pv;  // L >= 2 whenever a tile is scanned
+    if constexpr (APPEND) {
+        p1 = tok_at<true>(r, r.L - 1);
+        p2 = tok_at<true>(r, r.L - 2);
+        p3 = tok_at<true>(r, r.L - (mhat >= 3 ? 3 : 1));
+        pv = tok_at<true>(r, r.L - mhat + (lane < mhat ? lane : 0));
+    } else {
+        p1 = gld(r.h + r.L - 1);
+        p2 = gld(r.h + r.L - 2);
+        p3 = gld(r.h + r.L - (mhat >= 3 ? 3 : 1));
+        pv = gld(r.h + r.L - mhat + (lane < mhat ? lane : 0));
+    }
     if constexpr (PRELOADED) {
         // the caller issued this tile's loads before the length was known
     } else if constexpr (!CHECKED) {
@@ -497,14 +568,14 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
 #pragma unroll
         for (int k = 0; k <= kPer; ++k) {
             const int q = k < kPer ? kHaloChunks + k * kWave + lane : qx;
-            inside[k] = q >= 0 && chunk_inside(pq0 + 4 * q, r.L);
+            inside[k] = q >= 0 && chunk_inside(pq0 + 4 * q, APPEND ? r.split : r.L);
             v[k] = gld_stream(inside[k] ? arow + (gq0 + q) : a.zero16);
         }
 #pragma unroll
         for (int k = 0; k <= kPer; ++k) {
             const int q = k < kPer ? kHaloChunks + k * kWave + lane : qx;
             if (q >= 0 && !inside[k])
-                v[k] = patch_chunk(v[k], pq0 + 4 * q, r.h, r.L);
+                v[k] = patch_chunk<APPEND>(v[k], pq0 + 4 * q, r);
         }
     }
 
@@ -628,7 +699,15 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
 // caller's bound min_len (checked against each length on the device) then
 // issues its loads at once, before its length is read from memory; other
 // tiles, and row-table batches, read the length and row first.
-template <int TILE, int THREADS, bool STRIDED, bool FUSE, bool CONTROL>
+//
+// APPEND (a strided batch over the context's store, fused gather): row b
+// first gains counts[b] tokens, as pld_append would add them. Positions at
+// or past the old length are read from the append's source, so no
+// workgroup depends on the copy, which the request's last tile makes. The
+// new length is stored by the workgroup that emits the draft, and every
+// workgroup of the request (those without candidates too) counts itself in
+// before that, so none of them can read the new length as its old one.
+template <int TILE, int THREADS, bool STRIDED, bool FUSE, bool CONTROL, bool APPEND>
 __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int32_t *lengths,
                                                     int32_t batch, int32_t max_len,
                                                     int32_t n_min, int32_t n_max, int64_t stride,
@@ -667,7 +746,7 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
 
     int4 v[kPer + 1];
     bool ahead = false;
-    if constexpr (STRIDED) {
+    if constexpr (STRIDED && !APPEND) {
         // interior for every row of length >= min_len
         ahead = t0 >= kHalo + 4 && t0 + TILE + 4 <= (int64_t)min_len - 1;
         const int4 *arow = (const int4 *)(a.base + (int64_t)b * stride);
@@ -675,34 +754,50 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
         load_interior<TILE, THREADS>(arow, t0, ahead, arow, v);
     }
 
-    const Req r = load_req(a, b, TILE);
+    const Req r = load_req<APPEND>(a, b, TILE);
     FusePre pre{};
     if constexpr (FUSE)
         pre = fuse_preload(a.fuse, b, tid & (kWave - 1));
     CtlPre cpre{};
     if constexpr (CONTROL)
         cpre = control_preload(a.control, b, tid & (kWave - 1));
-    if (tile >= r.ntiles)
+    // workgroups counted in by the fused gather: the tiles that hold
+    // candidates, or with APPEND every tile of the request
+    const int32_t arrive = APPEND ? (int32_t)(gridDim.x / a.batch) : r.ntiles;
+    if (!APPEND && tile >= r.ntiles)
         return;  // this request has no candidates in this tile
-    if (r.err && tid == 0)
+    if (r.err && tid == 0 && (!APPEND || tile == 0))
         atomicOr(a.err, r.err);
+    if constexpr (APPEND) {
+        if (tile == 0 && tid == 0) {
+            if (r.app_err)
+                atomicOr(a.err, r.app_err);
+        }
+        // the copy; no workgroup of this launch reads these positions of the row
+        if (tile == r.ntiles - 1) {
+            int32_t *dst = a.app_store + (int64_t)b * a.stride + r.split;
+            for (int t = tid; t < r.add; t += THREADS)
+                dst[t] = gld(r.src + t);
+        }
+    }
 
     const int32_t mhat = r.L - 1 < a.n_max ? r.L - 1 : a.n_max;
     u64 best = 0;
-    if (mhat >= a.n_min) {
-        // interior: halo and the chunk after the tile lie inside the row and
-        // every position of the tile is a candidate
-        const bool interior = t0 >= kHalo + 4 && t0 + TILE + 4 <= (int64_t)r.L - 1;
+    if ((!APPEND || tile < r.ntiles) && mhat >= a.n_min) {
+        // interior: halo and the chunk after the tile lie inside the row (below
+        // the old length with APPEND) and every position of the tile is a
+        // candidate
+        const bool interior = t0 >= kHalo + 4 && t0 + TILE + 4 <= (int64_t)(APPEND ? r.split : r.L) - 1;
         const bool f3 = a.n_min >= 3;
-        if (STRIDED && ahead && r.err == 0)
-            best = f3 ? scan_wave<TILE, THREADS, false, true, true>(a, r, t0, mhat, win, pat, v)
-                      : scan_wave<TILE, THREADS, false, false, true>(a, r, t0, mhat, win, pat, v);
+        if (STRIDED && !APPEND && ahead && r.err == 0)
+            best = f3 ? scan_wave<TILE, THREADS, false, true, true, false>(a, r, t0, mhat, win, pat, v)
+                      : scan_wave<TILE, THREADS, false, false, true, false>(a, r, t0, mhat, win, pat, v);
         else if (interior)
-            best = f3 ? scan_wave<TILE, THREADS, false, true, false>(a, r, t0, mhat, win, pat, v)
-                      : scan_wave<TILE, THREADS, false, false, false>(a, r, t0, mhat, win, pat, v);
+            best = f3 ? scan_wave<TILE, THREADS, false, true, false, APPEND>(a, r, t0, mhat, win, pat, v)
+                      : scan_wave<TILE, THREADS, false, false, false, APPEND>(a, r, t0, mhat, win, pat, v);
         else
-            best = f3 ? scan_wave<TILE, THREADS, true, true, false>(a, r, t0, mhat, win, pat, v)
-                      : scan_wave<TILE, THREADS, true, false, false>(a, r, t0, mhat, win, pat, v);
+            best = f3 ? scan_wave<TILE, THREADS, true, true, false, APPEND>(a, r, t0, mhat, win, pat, v)
+                      : scan_wave<TILE, THREADS, true, false, false, APPEND>(a, r, t0, mhat, win, pat, v);
     }
 
     // 5. wavefront maximum by DPP (only in wavefronts that found a match),
@@ -734,14 +829,14 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
     if (tid == 0) {
         u64 m = wg_best;
         int last = 1;
-        if (r.ntiles > 1) {
+        if (arrive > 1) {
             if (m) {
                 __hip_atomic_fetch_max(&a.slots[b].key, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 wait_vm();
             }
             const unsigned prev = __hip_atomic_fetch_add(&a.slots[b].arrivals, 1u, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT);
-            last = prev == (unsigned)(r.ntiles - 1);
+            last = prev == (unsigned)(arrive - 1);
             if (last) {
                 m = __hip_atomic_exchange(&a.slots[b].key, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_exchange(&a.slots[b].arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -751,8 +846,15 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
         s_last = last;
     }
     __syncthreads();
-    if (s_last)
+    if (!s_last)
+        return;
+    if constexpr (APPEND) {
+        emit<true>(a, b, r, wg_best, tid, THREADS);
+        if (tid == 0 && r.add > 0)
+            a.app_lengths[b] = r.L;
+    } else {
         emit_request<FUSE, CONTROL>(a, b, r, wg_best, tid, THREADS, pre, cpre);
+    }
 }
 
 __global__ __launch_bounds__(kWave) void pld_gather(DraftArgs a)
@@ -782,17 +884,13 @@ __global__ __launch_bounds__(256) void pld_append_kernel(AppendArgs a)
     const int b = blockIdx.x;
     if (threadIdx.x == 0) {
         const int32_t len = a.lengths[b];
-        const int32_t c = a.counts[b];
-        int ok = 1;
-        if (c < 0) {
-            atomicOr(a.err, kErrAppendNegative);
-            ok = 0;
-        } else if ((int64_t)len + c > a.max_len) {
-            atomicOr(a.err, kErrAppendCapacity);
-            ok = 0;
-        }
+        // a length outside [0, max_len] (the array is the caller's to write
+        // through pld_store_views) rejects the append like an overflow
+        const uint32_t e = append_error(len, a.counts[b], a.max_len);
+        if (e)
+            atomicOr(a.err, e);
         s_len = len;
-        s_ok = ok;
+        s_ok = e == 0;
     }
     __syncthreads();
     if (!s_ok)
@@ -836,22 +934,29 @@ hipError_t launch_scan(const DraftArgs &a, int64_t tiles_per_req, hipStream_t s)
         return hipErrorInvalidValue;  // no entry point fuses a strided batch
     if (a.do_fuse && a.do_control)
         return hipErrorInvalidValue;  // no entry point does both
-    if (a.stride)
-        hipLaunchKernelGGL((pld_scan<TILE, THREADS, true, false, false>), dim3((unsigned)grid),
-                           dim3(THREADS), 0, s, (const void *)a.base, a.lengths, a.batch,
-                           a.max_len, a.n_min, a.n_max, a.stride, a.min_len, a);
+    if (a.do_append && (!a.stride || a.min_len != 0 || !a.fused || a.do_fuse || a.do_control))
+        return hipErrorInvalidValue;  // an append runs with the store's strided scan only
+    if (a.do_append)
+        hipLaunchKernelGGL((pld_scan<TILE, THREADS, true, false, false, true>),
+                           dim3((unsigned)grid), dim3(THREADS), 0, s, (const void *)a.base,
+                           a.lengths, a.batch, a.max_len, a.n_min, a.n_max, a.stride, 0, a);
+    else if (a.stride)
+        hipLaunchKernelGGL((pld_scan<TILE, THREADS, true, false, false, false>),
+                           dim3((unsigned)grid), dim3(THREADS), 0, s, (const void *)a.base,
+                           a.lengths, a.batch, a.max_len, a.n_min, a.n_max, a.stride, a.min_len,
+                           a);
     else if (a.do_fuse && a.fused)
-        hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, true, false>), dim3((unsigned)grid),
-                           dim3(THREADS), 0, s, (const void *)a.histories, a.lengths, a.batch,
-                           a.max_len, a.n_min, a.n_max, (int64_t)0, 0, a);
+        hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, true, false, false>),
+                           dim3((unsigned)grid), dim3(THREADS), 0, s, (const void *)a.histories,
+                           a.lengths, a.batch, a.max_len, a.n_min, a.n_max, (int64_t)0, 0, a);
     else if (a.do_control && a.fused)
-        hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, false, true>), dim3((unsigned)grid),
-                           dim3(THREADS), 0, s, (const void *)a.histories, a.lengths, a.batch,
-                           a.max_len, a.n_min, a.n_max, (int64_t)0, 0, a);
+        hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, false, true, false>),
+                           dim3((unsigned)grid), dim3(THREADS), 0, s, (const void *)a.histories,
+                           a.lengths, a.batch, a.max_len, a.n_min, a.n_max, (int64_t)0, 0, a);
     else
-        hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, false, false>), dim3((unsigned)grid),
-                           dim3(THREADS), 0, s, (const void *)a.histories, a.lengths, a.batch,
-                           a.max_len, a.n_min, a.n_max, (int64_t)0, 0, a);
+        hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, false, false, false>),
+                           dim3((unsigned)grid), dim3(THREADS), 0, s, (const void *)a.histories,
+                           a.lengths, a.batch, a.max_len, a.n_min, a.n_max, (int64_t)0, 0, a);
     return hipGetLastError();
 }
 
