@@ -143,13 +143,15 @@ __device__ __forceinline__ uint32_t append_error(int32_t len, int32_t c, int32_t
 
 // Row b is histories[b], or base + b * stride for a strided batch (a.stride
 // > 0, rows 16-byte aligned as checked on the host). With APPEND the row
-// first gains the counts[b] new tokens when that append is accepted.
+// first gains the counts[b] new tokens when that append is accepted, and
+// the batch is known to be strided.
 template <bool APPEND = false>
 __device__ __forceinline__ Req load_req(const DraftArgs &a, int b, int tile_tokens)
 {
     Req r;
     const int32_t old_len = a.lengths[b];
-    const int32_t *h = a.stride ? a.base + (int64_t)b * a.stride : a.histories[b];
+    const bool strided = APPEND || a.stride != 0;
+    const int32_t *h = strided ? a.base + (int64_t)b * a.stride : a.histories[b];
     r.add = 0;
     r.app_err = 0;
     if constexpr (APPEND) {
@@ -162,11 +164,11 @@ __device__ __forceinline__ Req load_req(const DraftArgs &a, int b, int tile_toke
     r.err = 0;
     if (len < 0)
         r.err |= kErrLenNegative;
-    else if (len > a.max_len || (a.stride && len > a.stride))
+    else if (len > a.max_len || (strided && len > a.stride))
         r.err |= kErrLenCapacity;
-    else if (a.stride && len < a.min_len)
+    else if (strided && len < a.min_len)
         r.err |= kErrBelowMinLen;
-    else if (!a.stride && len > 0 && (h == nullptr || ((uintptr_t)h & 3u)))
+    else if (!strided && len > 0 && (h == nullptr || ((uintptr_t)h & 3u)))
         r.err |= kErrBadRow;
     r.h = h;
     r.L = r.err ? 0 : len;
@@ -188,10 +190,14 @@ __device__ __forceinline__ Req load_req(const DraftArgs &a, int b, int tile_toke
 template <bool APPEND>
 __device__ __forceinline__ int32_t tok_at(const Req &r, int64_t p)
 {
-    if constexpr (APPEND)
-        return gld(p < r.split ? r.h + p : r.src + (p - r.split));
-    else
+    if constexpr (APPEND) {
+        // one of two uniform byte bases, then the position's offset
+        const uint64_t hb = (uint64_t)(uintptr_t)r.h;
+        const uint64_t sb = (uint64_t)(uintptr_t)r.src - 4 * (uint64_t)(uint32_t)r.split;
+        return gld((const int32_t *)(uintptr_t)((p < r.split ? hb : sb) + 4 * (uint64_t)p));
+    } else {
         return gld(r.h + p);
+    }
 }
 
 // Writes row b of the outputs from a packed key (0 = no match). Called by
@@ -434,25 +440,25 @@ __device__ __forceinline__ bool chunk_inside(int64_t p0, int32_t L)
     return p0 >= 0 && p0 + 3 < (int64_t)L;
 }
 
-// With APPEND a chunk is loaded whole only below the old length (the row
-// holds nothing newer yet), and the appended positions are patched in from
-// the append's source.
-template <bool APPEND>
-__device__ __forceinline__ int4 patch_chunk(int4 v, int64_t p0, const Req &r)
+__device__ __forceinline__ int4 patch_chunk(int4 v, int64_t p0, const int32_t *h, int32_t L)
+{
+    if (p0 + 0 >= 0 && p0 + 0 < L) v.x = gld(h + p0 + 0);
+    if (p0 + 1 >= 0 && p0 + 1 < L) v.y = gld(h + p0 + 1);
+    if (p0 + 2 >= 0 && p0 + 2 < L) v.z = gld(h + p0 + 2);
+    if (p0 + 3 >= 0 && p0 + 3 < L) v.w = gld(h + p0 + 3);
+    return v;
+}
+
+// The same with APPEND: a chunk is loaded whole only below the old length
+// (the row holds nothing newer yet); its other positions below the new
+// length come from the row or from the append's source, one load each.
+__device__ __forceinline__ int4 patch_chunk_append(int4 v, int64_t p0, const Req &r)
 {
     const int32_t L = r.L;
-    if constexpr (APPEND) {
-        if (p0 + 0 >= 0 && p0 + 0 < L) v.x = tok_at<true>(r, p0 + 0);
-        if (p0 + 1 >= 0 && p0 + 1 < L) v.y = tok_at<true>(r, p0 + 1);
-        if (p0 + 2 >= 0 && p0 + 2 < L) v.z = tok_at<true>(r, p0 + 2);
-        if (p0 + 3 >= 0 && p0 + 3 < L) v.w = tok_at<true>(r, p0 + 3);
-    } else {
-        const int32_t *h = r.h;
-        if (p0 + 0 >= 0 && p0 + 0 < L) v.x = gld(h + p0 + 0);
-        if (p0 + 1 >= 0 && p0 + 1 < L) v.y = gld(h + p0 + 1);
-        if (p0 + 2 >= 0 && p0 + 2 < L) v.z = gld(h + p0 + 2);
-        if (p0 + 3 >= 0 && p0 + 3 < L) v.w = gld(h + p0 + 3);
-    }
+    if (p0 + 0 >= 0 && p0 + 0 < L) v.x = tok_at<true>(r, p0 + 0);
+    if (p0 + 1 >= 0 && p0 + 1 < L) v.y = tok_at<true>(r, p0 + 1);
+    if (p0 + 2 >= 0 && p0 + 2 < L) v.z = tok_at<true>(r, p0 + 2);
+    if (p0 + 3 >= 0 && p0 + 3 < L) v.w = tok_at<true>(r, p0 + 3);
     return v;
 }
 
@@ -574,8 +580,12 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
 #pragma unroll
         for (int k = 0; k <= kPer; ++k) {
             const int q = k < kPer ? kHaloChunks + k * kWave + lane : qx;
-            if (q >= 0 && !inside[k])
-                v[k] = patch_chunk<APPEND>(v[k], pq0 + 4 * q, r);
+            if (q >= 0 && !inside[k]) {
+                if constexpr (APPEND)
+                    v[k] = patch_chunk_append(v[k], pq0 + 4 * q, r);
+                else
+                    v[k] = patch_chunk(v[k], pq0 + 4 * q, r.h, r.L);
+            }
         }
     }
 
@@ -763,7 +773,9 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
         cpre = control_preload(a.control, b, tid & (kWave - 1));
     // workgroups counted in by the fused gather: the tiles that hold
     // candidates, or with APPEND every tile of the request
-    const int32_t arrive = APPEND ? (int32_t)(gridDim.x / a.batch) : r.ntiles;
+    // (the grid holds this many tiles per request: launch_draft sizes it so)
+    const int32_t arrive = APPEND ? (a.max_len > 1 ? (int32_t)(((int64_t)a.max_len - 1 + TILE - 1) / TILE) : 1)
+                                  : r.ntiles;
     if (!APPEND && tile >= r.ntiles)
         return;  // this request has no candidates in this tile
     if (r.err && tid == 0 && (!APPEND || tile == 0))
