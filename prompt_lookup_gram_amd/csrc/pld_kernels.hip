@@ -57,6 +57,7 @@ constexpr int kHalo = 64;                 // >= PLD_N_MAX_LIMIT - 1, multiple of
 constexpr int kHaloChunks = kHalo / 4;    // 16-byte chunks of halo
 constexpr int kWave = 64;
 constexpr int kExtBlock = 4;             // tokens compared per LDS round trip when extending
+constexpr unsigned kGridY = 65535;       // largest y extent of a grid
 
 typedef unsigned long long u64;
 
@@ -750,9 +751,17 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
-    const int tile = blockIdx.x / a.batch;
-    const int b = blockIdx.x - tile * a.batch;
+    // grid: x = request, y = tile (and z, when a request has more tiles than
+    // the y dimension holds: y is then exactly kGridY tiles, and tile =
+    // z * kGridY + y). Workgroups are dispatched x-fastest, so consecutive
+    // ones hold the same tile of consecutive requests.
+    const int tile = (int)(blockIdx.z * kGridY + blockIdx.y);
+    const int b = blockIdx.x;
     const int64_t t0 = (int64_t)tile * TILE;
+    // tiles per request (the grid may hold a few more when split over z)
+    const int32_t req_tiles = a.max_len > 1 ? (int32_t)(((int64_t)a.max_len - 1 + TILE - 1) / TILE) : 1;
+    if (APPEND && tile >= req_tiles)
+        return;  // past every request's tiles: counts in nowhere, reads nothing
 
     int4 v[kPer + 1];
     bool ahead = false;
@@ -773,9 +782,7 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
         cpre = control_preload(a.control, b, tid & (kWave - 1));
     // workgroups counted in by the fused gather: the tiles that hold
     // candidates, or with APPEND every tile of the request
-    // (the grid holds this many tiles per request: launch_draft sizes it so)
-    const int32_t arrive = APPEND ? (a.max_len > 1 ? (int32_t)(((int64_t)a.max_len - 1 + TILE - 1) / TILE) : 1)
-                                  : r.ntiles;
+    const int32_t arrive = APPEND ? req_tiles : r.ntiles;
     if (!APPEND && tile >= r.ntiles)
         return;  // this request has no candidates in this tile
     if (r.err && tid == 0 && (!APPEND || tile == 0))
@@ -941,7 +948,9 @@ __global__ __launch_bounds__(kWave) void pld_fuse_kernel(FuseArgs a)
 template <int TILE, int THREADS>
 hipError_t launch_scan(const DraftArgs &a, int64_t tiles_per_req, hipStream_t s)
 {
-    const int64_t grid = tiles_per_req * a.batch;
+    // y holds at most kGridY tiles; more go on in z
+    const unsigned ty = tiles_per_req < kGridY ? (unsigned)tiles_per_req : kGridY;
+    const dim3 grid((unsigned)a.batch, ty, (unsigned)((tiles_per_req + ty - 1) / ty));
     if (a.stride && (a.do_fuse || a.do_control))
         return hipErrorInvalidValue;  // no entry point fuses a strided batch
     if (a.do_fuse && a.do_control)
@@ -950,24 +959,24 @@ hipError_t launch_scan(const DraftArgs &a, int64_t tiles_per_req, hipStream_t s)
         return hipErrorInvalidValue;  // an append runs with the store's strided scan only
     if (a.do_append)
         hipLaunchKernelGGL((pld_scan<TILE, THREADS, true, false, false, true>),
-                           dim3((unsigned)grid), dim3(THREADS), 0, s, (const void *)a.base,
+                           grid, dim3(THREADS), 0, s, (const void *)a.base,
                            a.lengths, a.batch, a.max_len, a.n_min, a.n_max, a.stride, 0, a);
     else if (a.stride)
         hipLaunchKernelGGL((pld_scan<TILE, THREADS, true, false, false, false>),
-                           dim3((unsigned)grid), dim3(THREADS), 0, s, (const void *)a.base,
+                           grid, dim3(THREADS), 0, s, (const void *)a.base,
                            a.lengths, a.batch, a.max_len, a.n_min, a.n_max, a.stride, a.min_len,
                            a);
     else if (a.do_fuse && a.fused)
         hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, true, false, false>),
-                           dim3((unsigned)grid), dim3(THREADS), 0, s, (const void *)a.histories,
+                           grid, dim3(THREADS), 0, s, (const void *)a.histories,
                            a.lengths, a.batch, a.max_len, a.n_min, a.n_max, (int64_t)0, 0, a);
     else if (a.do_control && a.fused)
         hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, false, true, false>),
-                           dim3((unsigned)grid), dim3(THREADS), 0, s, (const void *)a.histories,
+                           grid, dim3(THREADS), 0, s, (const void *)a.histories,
                            a.lengths, a.batch, a.max_len, a.n_min, a.n_max, (int64_t)0, 0, a);
     else
         hipLaunchKernelGGL((pld_scan<TILE, THREADS, false, false, false, false>),
-                           dim3((unsigned)grid), dim3(THREADS), 0, s, (const void *)a.histories,
+                           grid, dim3(THREADS), 0, s, (const void *)a.histories,
                            a.lengths, a.batch, a.max_len, a.n_min, a.n_max, (int64_t)0, 0, a);
     return hipGetLastError();
 }

@@ -321,3 +321,35 @@ def test_host_validation_enqueues_nothing():
         assert got_len.tolist() == [0, 0]
     finally:
         B.pld_destroy(ctx)
+
+
+def test_more_tiles_than_grid_rows():
+    """A capacity of 17,000,000 tokens at 256-token tiles needs 66,407 tiles
+    per request, more than one grid dimension holds: the tiles continue in a
+    third dimension. Short histories at the start of such rows, drafted by
+    the one-launch step and by the plain scan, match the oracle."""
+    import torch
+    nb, max_len = 2, 17_000_000
+    ctx = B.pld_create(nb, max_len, own_store=True)
+    try:
+        B.pld_configure(ctx, 256, 1)
+        mirror = Mirror(nb, max_len)
+        rng = np.random.default_rng(7303)
+        out = B.alloc_outputs(nb, 16)
+        for step in range(4):
+            tok = rng.integers(0, 5, (nb, 600)).astype(np.int32)
+            counts = np.array([600, 317], np.int32)
+            mirror.append(tok, counts, nb)
+            for t in out:
+                t.fill_(-7)
+            B.pld_append_draft_store(ctx, torch.from_numpy(tok).cuda(), 600,
+                                     torch.from_numpy(counts).cuda(), nb, 4, 12, 16, *out)
+            check_outputs(mirror, nb, 4, 12, 16, out, f"step {step}")
+        for t in out:
+            t.fill_(-7)
+        B.pld_draft_batch_pos(ctx, *B.pld_store_views(ctx), nb, 4, 12, 16, *out)
+        check_outputs(mirror, nb, 4, 12, 16, out, "plain scan")
+        assert B.pld_sync(ctx) == B.PLD_OK
+        check_store(ctx, mirror, nb, "store")
+    finally:
+        B.pld_destroy(ctx)
