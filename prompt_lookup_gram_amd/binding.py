@@ -484,7 +484,8 @@ class StridedBatch:
             buf[b, :len(h)] = h
         self.buf = torch.from_numpy(buf).to(device)
         self.lengths = torch.from_numpy(lens.astype(np.int32)).to(device)
-        self.min_len = int(lens.min(initial=0))
+        # the shortest history (0 for an empty batch): every row's length is at least this
+        self.min_len = int(lens.min()) if lens.size else 0
         self.max_len = max(1, need)
 
 

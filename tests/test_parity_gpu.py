@@ -453,6 +453,83 @@ def test_strided_fuzz(seed):
     assert_parity(w, got, f"strided min_len={min_len} stride={stride}")
 
 
+def pinned_batch(seed, L, batch=6, n_min=4, n_max=12, k_max=16):
+    """Rows of one length L over small alphabets (long, overlapping matches
+    anywhere, also across tile edges) and one large-alphabet row (usually no
+    match)."""
+    rng = np.random.default_rng([555, seed, L])
+    hs = []
+    for b in range(batch):
+        alpha = 151936 if b == batch - 1 else int(rng.integers(2, 6))
+        hs.append(rng.integers(0, alpha, L).astype(np.int32))
+    return wl.Workload(f"pinned{seed}_L{L}", hs, n_min, n_max, k_max)
+
+
+# a batch whose bounds pin every length (min_len equals the stride or
+# max_len): every tile loads before the length is read, and the stored length
+# is checked afterwards
+@pytest.mark.parametrize("L", [2, 3, 5, 13, 64, 67, 68, 69, 255, 256, 257, 1031, 4096, 4097,
+                               4100, 8195])
+@pytest.mark.parametrize("pin", ["stride", "max_len"])
+def test_strided_pinned_lengths(L, pin):
+    for n_min, tile, fused in ((4, 0, -1), (1, 256, 1), (2, 1024, 0), (3, 4096, 1)):
+        w = pinned_batch(n_min, L, n_min=n_min, n_max=max(n_min, 12))
+        if pin == "stride":
+            stride = -(-L // 4) * 4
+            if stride != L:
+                continue  # the stride is a multiple of 4: pinned through max_len only
+            st, got = run_strided(w, L, tile=tile, fused=fused, stride=stride, max_len=L + 100)
+        else:
+            st, got = run_strided(w, L, tile=tile, fused=fused, stride=-(-L // 4) * 4 + 8,
+                                  max_len=L)
+        assert st == B.PLD_OK
+        assert_parity(w, got, f"pinned by {pin} L={L} n_min={n_min} tile={tile} fused={fused}")
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("fused", [1, 0])
+def test_strided_pinned_every_tiling(tile, fused):
+    w = wl.ALL_CONFIGS[4]()
+    st, got = run_strided(w, int(w.lengths.min()), tile=tile, fused=fused)
+    assert st == B.PLD_OK
+    assert_parity(w, got, f"pinned tile={tile} fused={fused}")
+
+
+@pytest.mark.parametrize("fused", [1, 0])
+def test_strided_pinned_bad_stored_lengths(fused):
+    """With min_len equal to the stride, a stored length other than min_len
+    is an error: that row gets the no-match row and the error is reported;
+    the other rows are drafted as usual."""
+    L = 9000
+    w = pinned_batch(7, L, batch=5)
+    sb = B.StridedBatch(w.histories, stride=L)
+    od, ol, om, oj = oracle.draft(w.histories, w.n_min, w.n_max, w.k_max)
+    for bad, expect in ((L - 1, B.PLD_EINVAL), (-3, B.PLD_EINVAL), (L + 4, B.PLD_ECAPACITY)):
+        ctx = B.pld_create(w.batch, L + 64)
+        try:
+            B.pld_configure(ctx, 0, fused)
+            out = B.alloc_outputs(w.batch, w.k_max)
+            for t in out:
+                t.fill_(-7)
+            lens = sb.lengths.clone()
+            lens[2] = bad
+            B.pld_draft_batch_strided(ctx, sb.buf, sb.stride, lens, L, w.batch, w.n_min,
+                                      w.n_max, w.k_max, *out)
+            assert B.pld_sync(ctx) == expect
+            d, l, m, p = [t.cpu().numpy() for t in out]
+            assert (m[2], l[2], p[2]) == (0, 0, -1) and np.all(d[2] == -1)
+            for b in (0, 1, 3, 4):
+                assert (m[b], p[b], l[b]) == (om[b], oj[b], ol[b]), (bad, b)
+                assert np.array_equal(d[b], od[b])
+            # the slots were left clean: a second call with good lengths is exact
+            B.pld_draft_batch_strided(ctx, sb.buf, sb.stride, sb.lengths, L, w.batch,
+                                      w.n_min, w.n_max, w.k_max, *out)
+            assert B.pld_sync(ctx) == B.PLD_OK
+            assert_parity(w, [t.cpu().numpy() for t in out], f"after bad length {bad}")
+        finally:
+            B.pld_destroy(ctx)
+
+
 def test_strided_store_views_match_row_table():
     """The context's own store drafted through its row table and through a
     strided call over the same memory give the same outputs."""
