@@ -88,10 +88,11 @@ def parse():
     ap.add_argument("--config", type=int, default=4, choices=[1, 2, 3, 4, 5],
                     help="workload: 4 (default) is the 16 x 262,144 batch; 1-3 "
                          "the smaller batches; 5 the 1,024-step streaming decode")
-    ap.add_argument("--layout", choices=["strided", "rows"], default="strided",
-                    help="histories as one padded [batch, stride] buffer per copy "
-                         "(pld_draft_batch_strided, min_len = the shortest history) "
-                         "or through a row-pointer table (pld_draft_batch)")
+    ap.add_argument("--layout", choices=["strided", "rows"], default="rows",
+                    help="histories through a row-pointer table (pld_draft_batch, "
+                         "the default) or as one padded [batch, stride] buffer per "
+                         "copy (pld_draft_batch_strided, min_len = the shortest "
+                         "history)")
     ap.add_argument("--graph-steps", type=int, default=128,
                     help="draft calls captured per HIP graph")
     ap.add_argument("--latency-calls", type=int, default=2000)
@@ -318,7 +319,7 @@ def main():
     graph_us = gpu_ms * 1e3 / steps           # mean launch time (one kernel per step)
     scan_gbps = bytes_step / (graph_us * 1e-6) / 1e9
     default_launch = (args.tile in (0, 4096) and args.fused in (-1, 1)
-                      and args.layout == "strided")
+                      and args.layout == "rows")
     traffic = profiled_traffic(args.config) if default_launch else None
     rec = {
         "metric": METRIC,
