@@ -798,6 +798,18 @@ def bench_stream(args, torch, B, wl, dev):
         "hbm_frac": None if (args.index or args.ngram) else
             round(bytes_mean * steps_n / gpu_s / 1e9 / HBM_PEAK_GBPS, 4),
     }
+    if not (args.index or args.ngram):
+        # the whole step (the append and the scan, one or two launches) against
+        # the HBM peak: a lower bound of the scan kernel's own fraction
+        kernels = (["pld_scan"] + ([] if args.append_draft else ["pld_append_kernel"])
+                   + (["pld_control_kernel"] if args.control and not args.control_fused else []))
+        rec["roofline"] = {
+            "bound": "hbm", "achieved": rec["scan_GBps"], "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": rec["hbm_frac"], "traffic": None,
+            "kernel": " + ".join(kernels),
+            "time_source": f"HIP events around the replayed {steps_n}-step graph, whole step "
+                           f"({len(kernels)} launch{'es' if len(kernels) > 1 else ''}); "
+                           "bytes = the mean history bytes per step"}
     if args.ngram:
         # a different drafter: no history bytes are read per step
         rec["metric"] = METRIC_NGRAM
