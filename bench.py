@@ -18,7 +18,9 @@ Reported (one JSON line on stdout):
                 summary, used only while the kernel source still matches it.
   p50_us/p90_us latency of one call: HIP event pair around a single eager
                 call (this includes the event-pair overhead of the runtime).
-  cpu_baseline  the CPU oracle on the same batch, one thread.
+  cpu_baseline  the CPU oracle on the same batch, one thread; and, for
+                context, cpu_baseline_threads: the same oracle one request per
+                task over the host cores.
 """
 
 from __future__ import annotations
@@ -377,6 +379,28 @@ def main():
                       f"({el:.1f} s, one thread, {cpu_model()}, "
                       f"{len(os.sched_getaffinity(0))} host cores visible)",
             "effective_GBps": round(bytes_step * n / el / 1e9, 3),
+        }
+        # secondary, for context: the same oracle fanned out one request per
+        # task over the host cores (its C call releases the GIL)
+        from concurrent.futures import ThreadPoolExecutor
+        cores = len(os.sched_getaffinity(0))
+
+        def one(h):
+            oracle.draft([h], w.n_min, w.n_max, w.k_max)
+
+        with ThreadPoolExecutor(max_workers=cores) as ex:
+            n2, t2 = 0, time.perf_counter()
+            while True:
+                list(ex.map(one, w.histories))
+                n2 += 1
+                el2 = time.perf_counter() - t2
+                if el2 >= args.cpu_seconds / 2:
+                    break
+        rec["cpu_baseline_threads"] = {
+            "value": round(n2 / el2, 3), "unit": "draft steps/s",
+            "cores": min(cores, w.batch), "kind": "oracle",
+            "sample": f"{n2} full steps of the same batch, one request per task on a pool of "
+                      f"{cores} threads ({el2:.1f} s, {cpu_model()})",
         }
         rec["parity"] = "bit-exact" if parity else "MISMATCH"
         if not parity:
