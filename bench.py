@@ -17,7 +17,8 @@ Reported (one JSON line on stdout):
                 HBM bytes per launch from the committed rocprofv3 counter
                 summary, used only while the kernel source still matches it.
   p50_us/p90_us latency of one call: HIP event pair around a single eager
-                call (this includes the event-pair overhead of the runtime).
+                call (this includes the event-pair overhead of the runtime);
+                p50_GBps the history bytes over that median.
   cpu_baseline  the CPU oracle on the same batch, one thread; and, for
                 context, cpu_baseline_threads: the same oracle one request per
                 task over the host cores.
@@ -346,6 +347,8 @@ def main():
         "hbm_frac": round(scan_gbps / HBM_PEAK_GBPS, 4),
         "p50_us": round(p50, 3),
         "p90_us": round(p90, 3),
+        # the whole eager step at its median latency, launch included
+        "p50_GBps": round(bytes_step / (p50 * 1e-6) / 1e9, 1),
         "graph_us_per_step": round(graph_us, 3),
         "eager_call_mean_us": round(mean_us, 3),
         "roofline": {"bound": "hbm", "achieved": round(scan_gbps, 1),
