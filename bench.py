@@ -321,7 +321,13 @@ def main():
 
     graph_us = gpu_ms * 1e3 / steps           # mean launch time (one kernel per step)
     scan_gbps = bytes_step / (graph_us * 1e-6) / 1e9
-    default_launch = (args.tile in (0, 4096) and args.fused in (-1, 1)
+    # the library's automatic tile (tile 0): 4,096 when a request fits one
+    # such tile, else the largest of 4,096, 2,048 and 1,024 that gives the
+    # scan at least 1,024 workgroups
+    max_len = max(1, int(w.lengths.max()))
+    auto = 4096 if max_len - 1 <= 4096 else next(
+        (t for t in (4096, 2048) if w.batch * -(-(max_len - 1) // t) >= 1024), 1024)
+    default_launch = (args.tile in (0, auto) and args.fused in (-1, 1)
                       and args.layout == "rows")
     traffic = profiled_traffic(args.config) if default_launch else None
     rec = {
@@ -338,6 +344,7 @@ def main():
         "dtype": "int32",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "layout": args.layout,
+                   "tile_tokens": args.tile or auto,
                    "history_tokens": int(w.lengths.max()),
                    "n_min": w.n_min, "n_max": w.n_max, "k_max": w.k_max,
                    "bytes_per_step": bytes_step, "rotated_copies": rot,

@@ -108,7 +108,11 @@ pld_status pld_destroy(pld_ctx *ctx);
 /*
  * Tuning controls. They never change results, only how the scan is split:
  *  tile_tokens: candidate positions per workgroup, one of 256, 1024, 2048,
- *               4096 (default), 8192, 16384; 0 keeps the current value.
+ *               4096, 8192, 16384; -1 restores the default, chosen per call:
+ *               4096 when max_len fits one tile of 4096, else the largest of
+ *               4096, 2048 and 1024 that gives the scan at least 1024
+ *               workgroups (batch x tiles of max_len); 0 keeps the current
+ *               value.
  *  fused_gather: 1 (default) lets the last workgroup of each request emit
  *               its draft inside the scan kernel; 0 emits drafts with a
  *               second kernel; -1 keeps the current value.

@@ -18,7 +18,7 @@ struct pld_ctx {
     int device;
     int32_t max_batch;
     int32_t max_len;
-    int32_t tile_tokens;
+    int32_t tile_tokens;        // scan tile size; 0: chosen per call (pick_tile)
     int32_t fused;
     pld::ReqSlot *slots;        // [max_batch] reduction state
     unsigned int *err;          // one word
@@ -79,6 +79,24 @@ bool valid_tile(int32_t t)
 {
     return t == 256 || t == 1024 || t == 2048 || t == 4096 || t == 8192 || t == 16384;
 }
+// The scan's tile size for a call: the caller's choice, or automatically
+// the largest of 4,096, 2,048 and 1,024 candidate positions that still gives
+// the grid at least 1,024 workgroups (4 per compute unit), so that small
+// batches spread over the whole chip and large ones keep their workgroups
+// few. A request that fits one 4,096-token tile is not split: its single
+// workgroup emits without the cross-workgroup merge.
+static int32_t pick_tile(const pld_ctx *ctx, int32_t batch)
+{
+    if (ctx->tile_tokens != 0)
+        return ctx->tile_tokens;
+    if (pld::scan_grid(ctx->max_len, 1, 4096) <= 1)
+        return 4096;
+    for (int32_t t = 4096; t > 1024; t /= 2)
+        if (pld::scan_grid(ctx->max_len, batch, t) >= 1024)
+            return t;
+    return 1024;
+}
+
 
 pld_status check_draft_args(pld_ctx *ctx, const int32_t *const *histories,
                             const int32_t *lengths, int32_t batch, int32_t n_min,
@@ -101,7 +119,7 @@ pld_status check_draft_args(pld_ctx *ctx, const int32_t *const *histories,
         return fail(PLD_EINVAL, "lengths and outputs must be 4-byte aligned");
     if ((int64_t)batch * k_max > INT64_MAX / 4)
         return fail(PLD_EINVAL, "batch * k_max too large");
-    if (pld::scan_grid(ctx->max_len, batch, ctx->tile_tokens) > 0x7fffffffLL)
+    if (pld::scan_grid(ctx->max_len, batch, pick_tile(ctx, batch)) > 0x7fffffffLL)
         return fail(PLD_EINVAL, "grid too large: batch %d x tiles for max_len %d", batch,
                     ctx->max_len);
     return PLD_OK;
@@ -175,7 +193,7 @@ pld_status draft(pld_ctx *ctx, const int32_t *const *histories, const int32_t *b
     a.app_counts = append ? append->counts : nullptr;
     a.app_store = append ? ctx->store : nullptr;
     a.app_lengths = append ? ctx->store_len : nullptr;
-    hipError_t e = pld::launch_draft(a, ctx->tile_tokens, stream);
+    hipError_t e = pld::launch_draft(a, pick_tile(ctx, a.batch), stream);
     if (e != hipSuccess)
         return hip_fail(e, "draft kernel launch");
     return PLD_OK;
@@ -289,7 +307,7 @@ pld_status create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t own
     memset(c, 0, sizeof(*c));
     c->max_batch = max_batch;
     c->max_len = max_len;
-    c->tile_tokens = 4096;
+    c->tile_tokens = 0;  // automatic (pick_tile)
     c->fused = 1;
     hipError_t e = hipGetDevice(&c->device);
     if (e != hipSuccess) {
@@ -480,13 +498,14 @@ pld_status pld_configure(pld_ctx *ctx, int32_t tile_tokens, int32_t fused_gather
 {
     if (!ctx)
         return fail(PLD_EINVAL, "ctx is null");
-    if (tile_tokens != 0 && !valid_tile(tile_tokens))
-        return fail(PLD_EINVAL, "tile_tokens %d not one of 256, 1024, 2048, 4096, 8192, 16384",
+    if (tile_tokens != 0 && tile_tokens != -1 && !valid_tile(tile_tokens))
+        return fail(PLD_EINVAL,
+                    "tile_tokens %d not one of 256, 1024, 2048, 4096, 8192, 16384, 0 or -1",
                     tile_tokens);
     if (fused_gather < -1 || fused_gather > 1)
         return fail(PLD_EINVAL, "fused_gather must be -1, 0 or 1 (got %d)", fused_gather);
     if (tile_tokens != 0)
-        ctx->tile_tokens = tile_tokens;
+        ctx->tile_tokens = tile_tokens == -1 ? 0 : tile_tokens;
     if (fused_gather >= 0)
         ctx->fused = fused_gather;
     return PLD_OK;
