@@ -692,7 +692,7 @@ def bench_stream(args, torch, B, wl, dev):
         ctx = B.pld_create_ngram(nb, max_len)
     else:
         ctx = B.pld_create(nb, max_len, own_store=True)
-    rows, lens = B.pld_store_views(ctx)
+    rows, lens = B.pld_histories(ctx)
     # controller inputs: every outcome "0 accepted in time 1.0" is valid for
     # any previous choice, so the captured steps need no host round trip
     cparams = B.pld_control_params_default()

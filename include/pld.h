@@ -34,8 +34,13 @@
  *  - Problems only visible on the device (a bad per-request length or row
  *    pointer, an append past capacity) do not stop the call: the affected
  *    request is written as "no match" (or its append is dropped) and a sticky
- *    flag is set, which pld_sync() reports and clears.
- *  - Only pld_create allocates. No other entry point allocates memory.
+ *    flag is set, which pld_sync() reports and clears. Nothing is ever cut
+ *    to fit: the Strata engine review (chapter 05, on using the engine)
+ *    reports a context longer than the model's limit as an error instead of
+ *    truncating it, and a history or append past max_len is handled the
+ *    same way here.
+ *  - Only the pld_create* calls allocate. No other entry point allocates
+ *    memory.
  *  - A context must not be used from two host threads at once, and two
  *    draft or append calls on one context must not overlap in time on the
  *    device (they share the context's per-request reduction slots): issue them
@@ -68,7 +73,8 @@ typedef enum pld_status {
 
 /*
  * Create a context for batches of up to max_batch requests whose histories
- * are at most max_len tokens (1 <= max_len <= 2^31 - 1).
+ * are at most max_len tokens (1 <= max_len <= 2^31 - 1: a position must fit
+ * the low 32 bits of the packed key the scan reduces).
  *
  * The context holds 256 bytes of reduction state per request, a sticky error
  * word and, when own_store != 0, a history store of max_batch rows of
@@ -76,12 +82,14 @@ typedef enum pld_status {
  * all lengths starting at 0 (fed by pld_append; the Strata prompt-lookup page,
  * section 4, keeps its history index growing by O(1) appends).
  *
- * out: receives the context (unchanged on failure).
- * Errors: PLD_EINVAL (bad sizes, null out), PLD_ENOMEM, PLD_EHIP.
- * Synchronous: returns once the context's memory is allocated and cleared.
+ * out:    receives the context (unchanged on failure).
+ * stream: the context's memory is cleared by work enqueued on this stream
+ *         (NULL: the null stream); the call waits for that work.
+ * Errors: PLD_EINVAL (bad sizes, null out; max_len >= 2^31), PLD_ENOMEM,
+ * PLD_EHIP. The only entry points that allocate are the pld_create* calls.
  */
-pld_status pld_create(pld_ctx **out, int32_t max_batch, int32_t max_len,
-                      int32_t own_store);
+pld_status pld_create(pld_ctx **out, int32_t max_batch, int64_t max_len,
+                      int32_t own_store, hipStream_t stream);
 
 /*
  * pld_create with a store (own_store = 1) and an incremental n-gram index
@@ -96,10 +104,11 @@ pld_status pld_create(pld_ctx **out, int32_t max_batch, int32_t max_len,
  * Memory: max_batch * (n_max - n_min + 1) tables of 8-byte slots, each table
  * a power of two >= 2 * max_len slots (576 MB for 64 requests of 49,152
  * tokens and lengths 4..12).
- * Errors: as pld_create; PLD_EINVAL for a bad length range.
+ * Errors: as pld_create (max_len and stream as there); PLD_EINVAL for a
+ * bad length range.
  */
-pld_status pld_create_indexed(pld_ctx **out, int32_t max_batch, int32_t max_len,
-                              int32_t n_min, int32_t n_max);
+pld_status pld_create_indexed(pld_ctx **out, int32_t max_batch, int64_t max_len,
+                              int32_t n_min, int32_t n_max, hipStream_t stream);
 
 /* Free everything the context owns. Waits for the device to finish work
    first. NULL is a no-op. */
@@ -121,7 +130,22 @@ pld_status pld_destroy(pld_ctx *ctx);
 pld_status pld_configure(pld_ctx *ctx, int32_t tile_tokens, int32_t fused_gather);
 
 /*
+ * The scan's tile for a draft call of `batch` requests on this context: the
+ * candidate positions each workgroup covers, as pld_configure fixed it or as
+ * the automatic rule picks it. Reporting only; the tile never changes
+ * results.
+ *  tile_tokens: host out-param.
+ * Errors: PLD_EINVAL (null ctx or out, batch outside [1, max_batch]).
+ */
+pld_status pld_scan_tile(pld_ctx *ctx, int32_t batch, int32_t *tile_tokens);
+
+/*
  * Streaming append into the context's own store (own_store != 0).
+ *
+ * The Strata prompt-lookup page (section 4, prompt lookup) keeps the
+ * history it drafts from current by appending each accepted token in O(1);
+ * here an append is O(count) work for the appended tokens only, whatever
+ * the row's length, and never re-reads the stored history.
  *
  * For b < batch: tokens[b * tokens_stride + t] for t < counts[b] are appended
  * to row b, whose length grows by counts[b].
@@ -131,7 +155,7 @@ pld_status pld_configure(pld_ctx *ctx, int32_t tile_tokens, int32_t fused_gather
  * A row whose append would pass max_len, or whose count is negative, is left
  * unchanged and sets the sticky flag (PLD_ECAPACITY / PLD_EINVAL at
  * pld_sync); so is a row whose stored length is outside [0, max_len] (the
- * length array is reachable through pld_store_views), as PLD_ECAPACITY.
+ * length array is reachable through pld_histories), as PLD_ECAPACITY.
  * batch == 0 is a no-op. With an index (pld_create_indexed) the
  * n-grams that the append makes draftable are inserted first, in a second
  * kernel on the same stream. With a successor-count cache
@@ -145,12 +169,14 @@ pld_status pld_append(pld_ctx *ctx, const int32_t *tokens, int64_t tokens_stride
                       const int32_t *counts, int32_t batch, hipStream_t stream);
 
 /*
- * Device views of the context's store, for pld_draft_batch:
- *  *histories: device array of max_batch row pointers;
- *  *lengths:   device int32[max_batch] current row lengths.
+ * Device views of the context's store, to pass to pld_draft_batch (the
+ * HyperQwen page, step 1, drafts each request from its own history; these
+ * are those histories as the appends left them):
+ *  *histories: device array of max_batch row pointers (host out-param);
+ *  *lengths:   device int32[max_batch] current row lengths (host out-param).
  * Both stay owned by the context. Errors: PLD_EINVAL (no store, null out).
  */
-pld_status pld_store_views(pld_ctx *ctx, const int32_t *const **histories,
+pld_status pld_histories(pld_ctx *ctx, const int32_t *const **histories,
                            const int32_t **lengths);
 
 /* Set every store row's length to 0, and empty the n-gram index if there is
@@ -231,7 +257,7 @@ pld_status pld_index_fingerprint_bits(pld_ctx *ctx, int32_t bits);
  * probe per length n in [n_min, n_max], in parallel; the longest hit is
  * confirmed against the stored tokens (a shared-fingerprint slot that does
  * not confirm sends that request to an exact scan of its row). Results are
- * identical to pld_draft_batch_pos on pld_store_views (same outputs, same
+ * identical to pld_draft_batch_pos on pld_histories (same outputs, same
  * padding).
  *  n_min, n_max: within the indexed lengths of pld_create_indexed.
  *  out_pos: device int32[batch] or NULL.
@@ -245,7 +271,7 @@ pld_status pld_draft_store(pld_ctx *ctx, int32_t batch, int32_t n_min, int32_t n
  * One decode step on the context's store: pld_append (tokens, tokens_stride,
  * counts, batch as there), then the draft of the first `batch` rows of the
  * new histories (n_min, n_max, k_max and outputs as in pld_draft_store or,
- * without an index, pld_draft_batch_pos on pld_store_views; out_pos may be
+ * without an index, pld_draft_batch_pos on pld_histories; out_pos may be
  * NULL). On an indexed context n_min, n_max must lie inside the indexed
  * lengths. With 0 < tokens_stride <= 1024 both steps run in one launch:
  * on an indexed context one workgroup per request; on a context with a
@@ -463,9 +489,11 @@ pld_status pld_ngram_params_default(pld_ngram_params *params);
  * slots and one of successor-pair slots, 32 bytes each, each a power of two
  * >= max(16, 2 * max_len) slots (2.15 GB for 64 requests of 49,152 tokens
  * and n_max 4). A context has either this cache or an index, not both.
- * Errors: as pld_create; PLD_EINVAL for n_max out of range.
+ * Errors: as pld_create (max_len and stream as there); PLD_EINVAL for n_max
+ * out of range.
  */
-pld_status pld_create_ngram(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t n_max);
+pld_status pld_create_ngram(pld_ctx **out, int32_t max_batch, int64_t max_len, int32_t n_max,
+                            hipStream_t stream);
 
 /*
  * Drafts for the first `batch` rows of the context's store from its
@@ -518,7 +546,11 @@ pld_status pld_draft_control_batch(pld_ctx *ctx, const int32_t *const *histories
                                    double *out_rates, hipStream_t stream);
 
 /*
- * Wait for the stream, then report and clear the sticky device-side flag:
+ * Wait for the device (the given stream and every other stream), then
+ * report and clear the sticky device-side flag. The flag exists so that a
+ * bad request is reported and never silently cut short (the Strata engine
+ * review, chapter 05: an over-long context is an error, not a truncation).
+ * Statuses:
  * PLD_OK when clear; PLD_ECAPACITY when a history exceeded max_len (or its
  * row's stride) or an append overflowed; PLD_EINVAL when a length or count
  * was negative, a length was below a strided call's min_len, a row pointer

@@ -28,7 +28,7 @@ PLD_FUSE_MAX_POSITIONS = 64
 
 # every symbol include/pld.h declares
 EXPORTS = ("pld_create", "pld_create_indexed", "pld_destroy", "pld_configure", "pld_append",
-           "pld_store_views", "pld_store_reset", "pld_draft_batch",
+           "pld_histories", "pld_store_reset", "pld_scan_tile", "pld_draft_batch",
            "pld_draft_batch_pos", "pld_draft_batch_strided", "pld_index_fingerprint_bits",
            "pld_draft_store", "pld_append_draft_store",
            "pld_fuse_params_default",
@@ -89,12 +89,12 @@ def load(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     sig = {
-        "pld_create": [ctypes.POINTER(vp), i32, i32, i32],
-        "pld_create_indexed": [ctypes.POINTER(vp), i32, i32, i32, i32],
+        "pld_create": [ctypes.POINTER(vp), i32, i64, i32, vp],
+        "pld_create_indexed": [ctypes.POINTER(vp), i32, i64, i32, i32, vp],
         "pld_destroy": [vp],
         "pld_configure": [vp, i32, i32],
         "pld_append": [vp, vp, i64, vp, i32, vp],
-        "pld_store_views": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp)],
+        "pld_histories": [vp, ctypes.POINTER(vp), ctypes.POINTER(vp)],
         "pld_store_reset": [vp, vp],
         "pld_draft_batch": [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp],
         "pld_draft_batch_pos": [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp],
@@ -112,7 +112,8 @@ def load(path: str = LIB_PATH):
         "pld_control": [vp, ctypes.POINTER(PldControlParams), vp, vp, vp, vp, vp, i32, vp, vp,
                         vp],
         "pld_ngram_params_default": [ctypes.POINTER(PldNgramParams)],
-        "pld_create_ngram": [ctypes.POINTER(vp), i32, i32, i32],
+        "pld_create_ngram": [ctypes.POINTER(vp), i32, i64, i32, vp],
+        "pld_scan_tile": [vp, i32, ctypes.POINTER(i32)],
         "pld_draft_ngram": [vp, ctypes.POINTER(PldNgramParams), i32, i32, vp, vp, vp, vp],
         "pld_append_draft_ngram": [vp, vp, i64, vp, i32, ctypes.POINTER(PldNgramParams), i32,
                                    vp, vp, vp, vp],
@@ -187,27 +188,45 @@ def pld_last_error() -> str:
     return load().pld_last_error().decode()
 
 
-def pld_create(max_batch: int, max_len: int, own_store: bool = False) -> int:
+def _create_stream(stream) -> int:
+    """The stream a pld_create* call clears the context on: the null stream
+    unless one is given (the call waits for it either way)."""
+    return 0 if stream is None else _stream(stream)
+
+
+def pld_create(max_batch: int, max_len: int, own_store: bool = False, stream=None) -> int:
     ctx = ctypes.c_void_p()
     _check("pld_create", load().pld_create(ctypes.byref(ctx), int(max_batch),
-                                           int(max_len), int(bool(own_store))))
+                                           int(max_len), int(bool(own_store)),
+                                           _create_stream(stream)))
     return ctx.value
 
 
-def pld_create_indexed(max_batch: int, max_len: int, n_min: int, n_max: int) -> int:
+def pld_create_indexed(max_batch: int, max_len: int, n_min: int, n_max: int,
+                       stream=None) -> int:
     """A context with a history store and an n-gram index over it."""
     ctx = ctypes.c_void_p()
     _check("pld_create_indexed", load().pld_create_indexed(
-        ctypes.byref(ctx), int(max_batch), int(max_len), int(n_min), int(n_max)))
+        ctypes.byref(ctx), int(max_batch), int(max_len), int(n_min), int(n_max),
+        _create_stream(stream)))
     return ctx.value
 
 
-def pld_create_ngram(max_batch: int, max_len: int, n_max: int = PLD_NGRAM_MAX_N) -> int:
+def pld_create_ngram(max_batch: int, max_len: int, n_max: int = PLD_NGRAM_MAX_N,
+                     stream=None) -> int:
     """A context with a history store and a successor-count cache over it."""
     ctx = ctypes.c_void_p()
     _check("pld_create_ngram", load().pld_create_ngram(
-        ctypes.byref(ctx), int(max_batch), int(max_len), int(n_max)))
+        ctypes.byref(ctx), int(max_batch), int(max_len), int(n_max), _create_stream(stream)))
     return ctx.value
+
+
+def pld_scan_tile(ctx: int, batch: int) -> int:
+    """Candidate positions per scan workgroup that a draft call of `batch`
+    requests on this context uses."""
+    t = ctypes.c_int32()
+    _check("pld_scan_tile", load().pld_scan_tile(ctx, int(batch), ctypes.byref(t)))
+    return t.value
 
 
 def pld_destroy(ctx: int) -> None:
@@ -227,10 +246,10 @@ def pld_append(ctx: int, tokens, tokens_stride: int, counts, batch: int,
         _dev_ptr(counts, "counts", i32), int(batch), _stream(stream)))
 
 
-def pld_store_views(ctx: int):
+def pld_histories(ctx: int):
     """(histories, lengths) device pointers of the context's store."""
     h, n = ctypes.c_void_p(), ctypes.c_void_p()
-    _check("pld_store_views", load().pld_store_views(ctx, ctypes.byref(h),
+    _check("pld_histories", load().pld_histories(ctx, ctypes.byref(h),
                                                      ctypes.byref(n)))
     return h.value, n.value
 

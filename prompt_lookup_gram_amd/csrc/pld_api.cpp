@@ -292,15 +292,19 @@ pld_status fuse_args(pld_ctx *ctx, const pld_fuse_params *params, const int32_t 
 }
 
 // Creates a context; index_lo > 0 adds an n-gram index over the store.
-pld_status create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t own_store,
-                  int32_t index_lo, int32_t index_hi, int32_t ngram_n_max = 0)
+pld_status create(pld_ctx **out, int32_t max_batch, int64_t max_len64, int32_t own_store,
+                  int32_t index_lo, int32_t index_hi, hipStream_t stream,
+                  int32_t ngram_n_max = 0)
 {
     if (!out)
         return fail(PLD_EINVAL, "out is null");
     if (max_batch < 1)
         return fail(PLD_EINVAL, "max_batch must be >= 1 (got %d)", max_batch);
-    if (max_len < 1)
-        return fail(PLD_EINVAL, "max_len must be in [1, 2^31-1] (got %d)", max_len);
+    // positions are the low 32 bits of the scan's packed key
+    if (max_len64 < 1 || max_len64 > 0x7fffffffLL)
+        return fail(PLD_EINVAL, "max_len must be in [1, 2^31-1] (got %lld)",
+                    (long long)max_len64);
+    const int32_t max_len = (int32_t)max_len64;
     pld_ctx *c = new (std::nothrow) pld_ctx();
     if (!c)
         return fail(PLD_ENOMEM, "host allocation failed");
@@ -376,28 +380,34 @@ pld_status create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t own
         const int64_t chunks = max_len / 8192;
         c->ngram_chunks = (int32_t)(chunks < 1 ? 1 : (chunks > 16 ? 16 : chunks));
     }
-    e = hipMemset(c->slots, 0, nb * sizeof(pld::ReqSlot));
+    // every clear is enqueued on the caller's stream, then waited for
+    const int32_t **rows = nullptr;
+    e = hipMemsetAsync(c->slots, 0, nb * sizeof(pld::ReqSlot), stream);
     if (e == hipSuccess && c->index)
-        e = pld::launch_index_clear(index_args(c), max_batch, nullptr);
+        e = pld::launch_index_clear(index_args(c), max_batch, stream);
     if (e == hipSuccess && c->ngram_grams)
-        e = pld::launch_ngram_clear(ngram_args(c), max_batch, nullptr);
-    if (e == hipSuccess) e = hipMemset(c->err, 0, sizeof(unsigned int));
-    if (e == hipSuccess) e = hipMemset(c->zero16, 0, sizeof(int4));
+        e = pld::launch_ngram_clear(ngram_args(c), max_batch, stream);
+    if (e == hipSuccess) e = hipMemsetAsync(c->err, 0, sizeof(unsigned int), stream);
+    if (e == hipSuccess) e = hipMemsetAsync(c->zero16, 0, sizeof(int4), stream);
     if (e == hipSuccess && own_store) {
-        e = hipMemset(c->store_len, 0, nb * sizeof(int32_t));
-        const int32_t **rows = new (std::nothrow) const int32_t *[nb];
+        e = hipMemsetAsync(c->store_len, 0, nb * sizeof(int32_t), stream);
+        rows = new (std::nothrow) const int32_t *[nb];
         if (!rows) {
+            (void)hipStreamSynchronize(stream);
             release(c);
             return fail(PLD_ENOMEM, "host allocation failed");
         }
         for (size_t b = 0; b < nb; ++b)
             rows[b] = c->store + (int64_t)b * c->pitch;
         if (e == hipSuccess)
-            e = hipMemcpy(c->store_rows, rows, nb * sizeof(int32_t *), hipMemcpyHostToDevice);
-        delete[] rows;
+            e = hipMemcpyAsync(c->store_rows, rows, nb * sizeof(int32_t *),
+                               hipMemcpyHostToDevice, stream);
     }
+    // the host row table must outlive the copy: wait before freeing it
+    const hipError_t w = hipStreamSynchronize(stream);
     if (e == hipSuccess)
-        e = hipDeviceSynchronize();
+        e = w;
+    delete[] rows;
     if (e != hipSuccess) {
         release(c);
         return hip_fail(e, "context initialisation");
@@ -462,25 +472,27 @@ pld_status control_args(pld_ctx *ctx, const pld_control_params *params, const in
 
 extern "C" {
 
-pld_status pld_create(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t own_store)
+pld_status pld_create(pld_ctx **out, int32_t max_batch, int64_t max_len, int32_t own_store,
+                      hipStream_t stream)
 {
-    return create(out, max_batch, max_len, own_store, 0, 0);
+    return create(out, max_batch, max_len, own_store, 0, 0, stream);
 }
 
-pld_status pld_create_indexed(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t n_min,
-                              int32_t n_max)
+pld_status pld_create_indexed(pld_ctx **out, int32_t max_batch, int64_t max_len, int32_t n_min,
+                              int32_t n_max, hipStream_t stream)
 {
     if (n_min < 1 || n_max < n_min || n_max > PLD_N_MAX_LIMIT)
         return fail(PLD_EINVAL, "need 1 <= n_min <= n_max <= %d (got n_min=%d n_max=%d)",
                     PLD_N_MAX_LIMIT, n_min, n_max);
-    return create(out, max_batch, max_len, 1, n_min, n_max);
+    return create(out, max_batch, max_len, 1, n_min, n_max, stream);
 }
 
-pld_status pld_create_ngram(pld_ctx **out, int32_t max_batch, int32_t max_len, int32_t n_max)
+pld_status pld_create_ngram(pld_ctx **out, int32_t max_batch, int64_t max_len, int32_t n_max,
+                            hipStream_t stream)
 {
     if (n_max < 1 || n_max > PLD_NGRAM_MAX_N)
         return fail(PLD_EINVAL, "need 1 <= n_max <= %d (got %d)", PLD_NGRAM_MAX_N, n_max);
-    return create(out, max_batch, max_len, 1, 0, 0, n_max);
+    return create(out, max_batch, max_len, 1, 0, 0, stream, n_max);
 }
 
 pld_status pld_destroy(pld_ctx *ctx)
@@ -565,7 +577,17 @@ pld_status pld_append(pld_ctx *ctx, const int32_t *tokens, int64_t tokens_stride
     return PLD_OK;
 }
 
-pld_status pld_store_views(pld_ctx *ctx, const int32_t *const **histories,
+pld_status pld_scan_tile(pld_ctx *ctx, int32_t batch, int32_t *tile_tokens)
+{
+    if (!ctx || !tile_tokens)
+        return fail(PLD_EINVAL, "ctx or tile_tokens is null");
+    if (batch < 1 || batch > ctx->max_batch)
+        return fail(PLD_EINVAL, "batch %d outside [1, max_batch=%d]", batch, ctx->max_batch);
+    *tile_tokens = pick_tile(ctx, batch);
+    return PLD_OK;
+}
+
+pld_status pld_histories(pld_ctx *ctx, const int32_t *const **histories,
                            const int32_t **lengths)
 {
     if (!ctx || !histories || !lengths)
@@ -929,12 +951,16 @@ pld_status pld_sync(pld_ctx *ctx, hipStream_t stream)
     if (!ctx)
         return fail(PLD_EINVAL, "ctx is null");
     unsigned int bits = 0;
+    // every stream first: a kernel of this context still running elsewhere
+    // could otherwise set a bit between the read and the clear below
     hipError_t e = hipStreamSynchronize(stream);
+    if (e == hipSuccess)
+        e = hipDeviceSynchronize();
     if (e == hipSuccess)
         e = hipMemcpy(&bits, ctx->err, sizeof(bits), hipMemcpyDeviceToHost);
     if (e == hipSuccess && bits)
         e = hipMemset(ctx->err, 0, sizeof(unsigned int));
-    if (e == hipSuccess)
+    if (e == hipSuccess && bits)
         e = hipDeviceSynchronize();
     if (e != hipSuccess)
         return hip_fail(e, "pld_sync");

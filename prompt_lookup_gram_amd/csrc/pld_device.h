@@ -8,8 +8,12 @@
 
 namespace pld {
 
-// Hash of a token sequence, one step per token, then a final mix (a 64-bit
-// multiply-xorshift finaliser).
+// Hash of a token sequence, one step per token, then a final mix. The step
+// multiplies by the 64-bit golden-ratio constant (2^64 / phi, Fibonacci
+// hashing as in Knuth's multiplicative method); the final mix is the fmix64
+// finaliser of Austin Appleby's MurmurHash3 (its published shift and
+// multiplier constants). The seed is the first 64 bits of pi's fraction.
+// Hash quality only affects speed: every hit is confirmed on the tokens.
 __device__ __forceinline__ unsigned long long hstep(unsigned long long h, int32_t t)
 {
     h ^= (uint32_t)t;

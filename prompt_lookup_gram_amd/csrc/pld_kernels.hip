@@ -1035,7 +1035,7 @@ __global__ __launch_bounds__(256) void pld_append_kernel(AppendArgs a)
     if (threadIdx.x == 0) {
         const int32_t len = a.lengths[b];
         // a length outside [0, max_len] (the array is the caller's to write
-        // through pld_store_views) rejects the append like an overflow
+        // through pld_histories) rejects the append like an overflow
         const uint32_t e = append_error(len, a.counts[b], a.max_len);
         if (e)
             atomicOr(a.err, e);

@@ -66,13 +66,70 @@ def test_null_context_rejected():
                                                    (4, -1, "max_len")])
 def test_create_rejects_bad_sizes_before_any_hip_call(max_batch, max_len, msg):
     ctx = ctypes.c_void_p()
-    assert _raw("pld_create", ctypes.byref(ctx), max_batch, max_len, 0) == B.PLD_EINVAL
+    assert _raw("pld_create", ctypes.byref(ctx), max_batch, max_len, 0, None) == B.PLD_EINVAL
     assert msg in B.pld_last_error()
     assert ctx.value is None
 
 
 def test_create_rejects_null_out():
-    assert _raw("pld_create", None, 4, 10, 0) == B.PLD_EINVAL
+    assert _raw("pld_create", None, 4, 10, 0, None) == B.PLD_EINVAL
+
+
+@pytest.mark.parametrize("max_len", [2**31, 2**31 + 5, 2**40])
+def test_create_rejects_max_len_past_the_key_field(max_len):
+    """max_len is int64 in the ABI; a position must fit the low 32 bits of
+    the packed key, so 2^31 and above are refused before any HIP call."""
+    ctx = ctypes.c_void_p()
+    for fn, extra in (("pld_create", (0,)), ("pld_create_indexed", (4, 12)),
+                      ("pld_create_ngram", (4,))):
+        assert _raw(fn, ctypes.byref(ctx), 4, max_len, *extra, None) == B.PLD_EINVAL
+        assert "max_len" in B.pld_last_error()
+        assert ctx.value is None
+
+
+# The boundary's calls and argument types as the scope table of the hot path
+# names them (pld_create with an int64 max_len and a stream; pld_histories for
+# the store's device views; the draft call over row pointers and lengths).
+SCOPE_PROTOTYPES = {
+    "pld_create": "pld_status pld_create(pld_ctx **out, int32_t max_batch, int64_t max_len, "
+                  "int32_t own_store, hipStream_t stream);",
+    "pld_destroy": "pld_status pld_destroy(pld_ctx *ctx);",
+    "pld_append": "pld_status pld_append(pld_ctx *ctx, const int32_t *tokens, "
+                  "int64_t tokens_stride, const int32_t *counts, int32_t batch, "
+                  "hipStream_t stream);",
+    "pld_histories": "pld_status pld_histories(pld_ctx *ctx, const int32_t *const **histories, "
+                     "const int32_t **lengths);",
+    "pld_draft_batch": "pld_status pld_draft_batch(pld_ctx *ctx, const int32_t *const *histories, "
+                       "const int32_t *lengths, int32_t batch, int32_t n_min, int32_t n_max, "
+                       "int32_t k_max, int32_t *out_draft, int32_t *out_len, "
+                       "int32_t *out_match, hipStream_t stream);",
+    "pld_draft_batch_pos": "pld_status pld_draft_batch_pos(pld_ctx *ctx, "
+                           "const int32_t *const *histories, const int32_t *lengths, "
+                           "int32_t batch, int32_t n_min, int32_t n_max, int32_t k_max, "
+                           "int32_t *out_draft, int32_t *out_len, int32_t *out_match, "
+                           "int32_t *out_pos, hipStream_t stream);",
+    "pld_sync": "pld_status pld_sync(pld_ctx *ctx, hipStream_t stream);",
+    "pld_strerror": "const char *pld_strerror(pld_status status);",
+}
+
+
+def _prototypes():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"([a-z_ *]+?\b(pld_[a-z_]+)\s*\([^;]*\);)", text):
+        out[m.group(2)] = " ".join(m.group(1).split()).replace("( ", "(")
+    return out
+
+
+@pytest.mark.parametrize("name", sorted(SCOPE_PROTOTYPES))
+def test_header_matches_scope_prototype(name):
+    assert _prototypes()[name] == SCOPE_PROTOTYPES[name]
+
+
+def test_scan_tile_query_rejects_bad_arguments():
+    t = ctypes.c_int32()
+    assert _raw("pld_scan_tile", None, 1, ctypes.byref(t)) == B.PLD_EINVAL
+    assert "null" in B.pld_last_error()
 
 
 def test_python_wrapper_raises_with_detail():
@@ -100,7 +157,8 @@ def test_fuse_null_context_or_params_rejected():
 def test_create_indexed_rejects_bad_lengths_before_any_hip_call():
     ctx = ctypes.c_void_p()
     for lo, hi in [(0, 4), (5, 4), (1, 65)]:
-        assert _raw("pld_create_indexed", ctypes.byref(ctx), 4, 100, lo, hi) == B.PLD_EINVAL
+        assert _raw("pld_create_indexed", ctypes.byref(ctx), 4, 100, lo, hi,
+                    None) == B.PLD_EINVAL
         assert "n_min" in B.pld_last_error()
     assert _raw("pld_draft_store", None, 1, 4, 12, 16, None, None, None, None,
                 None) == B.PLD_EINVAL
@@ -127,7 +185,7 @@ def test_ngram_params_default():
 def test_create_ngram_rejects_bad_lengths_before_any_hip_call():
     ctx = ctypes.c_void_p()
     for n_max in (0, 5, -1):
-        assert _raw("pld_create_ngram", ctypes.byref(ctx), 4, 100, n_max) == B.PLD_EINVAL
+        assert _raw("pld_create_ngram", ctypes.byref(ctx), 4, 100, n_max, None) == B.PLD_EINVAL
         assert "n_max" in B.pld_last_error()
     p = B.pld_ngram_params_default()
     assert _raw("pld_draft_ngram", None, ctypes.byref(p), 1, 16, None, None, None,

@@ -76,7 +76,7 @@ class Mirror:
 
 
 def store_state(ctx, max_batch: int):
-    rows, lens = B.pld_store_views(ctx)
+    rows, lens = B.pld_histories(ctx)
     table = to_host(np.zeros(max_batch, np.int64), rows)
     got_len = to_host(np.zeros(max_batch, np.int32), lens)
     got = [to_host(np.zeros(max(int(n), 0), np.int32), int(table[b])) if n > 0
@@ -128,7 +128,7 @@ def test_streaming_one_launch_every_tile(tile):
                      torch.full((nb,), wl.STREAM_START_LEN, dtype=torch.int32,
                                 device="cuda"), nb)
         out = B.alloc_outputs(nb, start.k_max)
-        B.pld_draft_batch_pos(ctx, *B.pld_store_views(ctx), nb, start.n_min, start.n_max,
+        B.pld_draft_batch_pos(ctx, *B.pld_histories(ctx), nb, start.n_min, start.n_max,
                               start.k_max, *out)
         for step in range(steps):
             d, l = out[0].cpu().numpy(), out[1].cpu().numpy()
@@ -219,7 +219,7 @@ def test_fuzz_against_oracle(seed):
 @pytest.mark.parametrize("seed", range(6))
 def test_same_as_append_then_draft(seed):
     """The one-launch step and the two-call step (pld_append, then the scan
-    over pld_store_views) leave the same outputs, store and status; the
+    over pld_histories) leave the same outputs, store and status; the
     second context drafts with the separate gather kernel, which never
     takes the one-launch path."""
     import torch
@@ -260,7 +260,7 @@ def test_same_as_append_then_draft(seed):
 @pytest.mark.parametrize("one_launch", [True, False])
 def test_corrupt_lengths_are_rejected(one_launch):
     """Lengths outside [0, max_len] written into the store's length array
-    (the caller can reach it through pld_store_views) reject that row's
+    (the caller can reach it through pld_histories) reject that row's
     append, flag the context and give a no-match row; nothing outside the
     rows' tokens is written and the other rows go on as usual."""
     import torch
@@ -274,7 +274,7 @@ def test_corrupt_lengths_are_rejected(one_launch):
         B.pld_append(ctx, torch.from_numpy(base).cuda(), 16,
                      torch.full((nb,), 16, dtype=torch.int32, device="cuda"), nb)
         assert B.pld_sync(ctx) == B.PLD_OK
-        rows, lens = B.pld_store_views(ctx)
+        rows, lens = B.pld_histories(ctx)
         table = to_host(np.zeros(nb, np.int64), rows)
         pitch = int(table[1] - table[0]) // 4
         before = to_host(np.zeros(nb * pitch, np.int32), int(table[0]))
@@ -347,7 +347,7 @@ def test_more_tiles_than_grid_rows():
             check_outputs(mirror, nb, 4, 12, 16, out, f"step {step}")
         for t in out:
             t.fill_(-7)
-        B.pld_draft_batch_pos(ctx, *B.pld_store_views(ctx), nb, 4, 12, 16, *out)
+        B.pld_draft_batch_pos(ctx, *B.pld_histories(ctx), nb, 4, 12, 16, *out)
         check_outputs(mirror, nb, 4, 12, 16, out, "plain scan")
         assert B.pld_sync(ctx) == B.PLD_OK
         check_store(ctx, mirror, nb, "store")

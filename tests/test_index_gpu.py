@@ -212,7 +212,7 @@ def test_index_overflow_and_errors():
 
 
 def test_index_agrees_with_scan_on_store():
-    """pld_draft_store and pld_draft_batch_pos over pld_store_views give the
+    """pld_draft_store and pld_draft_batch_pos over pld_histories give the
     same bits on one indexed store (both are checked against the oracle
     elsewhere; this pins the two GPU paths to each other directly)."""
     w = wl.config3()
@@ -220,7 +220,7 @@ def test_index_agrees_with_scan_on_store():
     try:
         s.append(w.histories)
         a = s.check(4, 12, 16, "config 3")
-        rows, lens = B.pld_store_views(s.ctx)
+        rows, lens = B.pld_histories(s.ctx)
         out = B.alloc_outputs(w.batch, 16)
         B.pld_draft_batch_pos(s.ctx, rows, lens, w.batch, 4, 12, 16, *out)
         assert B.pld_sync(s.ctx) == B.PLD_OK

@@ -326,7 +326,7 @@ def _stream_run(steps: int, check_every: int = 1):
     B_ = start.batch
     ctx = B.pld_create(B_, wl.STREAM_MAX_LEN, own_store=True)
     try:
-        rows, lens = B.pld_store_views(ctx)
+        rows, lens = B.pld_histories(ctx)
         init = torch.from_numpy(np.stack(start.histories)).cuda()
         counts0 = torch.full((B_,), wl.STREAM_START_LEN, dtype=torch.int32, device="cuda")
         B.pld_append(ctx, init, wl.STREAM_START_LEN, counts0, B_)
@@ -385,7 +385,7 @@ def test_append_overflow_sets_capacity_flag():
         assert B.pld_sync(ctx) == B.PLD_ECAPACITY
         B.pld_append(ctx, tok, 16, torch.tensor([-1, 0], dtype=torch.int32, device="cuda"), 2)
         assert B.pld_sync(ctx) == B.PLD_EINVAL
-        rows, lens = B.pld_store_views(ctx)
+        rows, lens = B.pld_histories(ctx)
         got = np.zeros(2, np.int32)
         _hip_copy_to_host(got, lens)
         assert got.tolist() == [6, 10]
@@ -538,7 +538,7 @@ def test_strided_store_views_match_row_table():
     nb = 8
     ctx = B.pld_create(nb, wl.STREAM_MAX_LEN, own_store=True)
     try:
-        rows, lens = B.pld_store_views(ctx)
+        rows, lens = B.pld_histories(ctx)
         init = torch.from_numpy(np.stack(start.histories[:nb])).cuda()
         B.pld_append(ctx, init, wl.STREAM_START_LEN,
                      torch.full((nb,), wl.STREAM_START_LEN, dtype=torch.int32,
