@@ -40,7 +40,7 @@
  *    truncating it, and a history or append past max_len is handled the
  *    same way here.
  *  - Only the pld_create* calls allocate. No other entry point allocates
- *    memory.
+ *    memory (pld_draft_batch_noalloc needs no context at all).
  *  - A context must not be used from two host threads at once, and two
  *    draft or append calls on one context must not overlap in time on the
  *    device (they share the context's per-request reduction slots): issue them
@@ -215,6 +215,39 @@ pld_status pld_draft_batch_pos(pld_ctx *ctx, const int32_t *const *histories,
                                int32_t *out_draft, int32_t *out_len,
                                int32_t *out_match, int32_t *out_pos,
                                hipStream_t stream);
+
+/*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): pld_draft_batch_pos
+ * without a context. The per-request reduction state lives in a static
+ * device array of the library instead of a context: 256 bytes for each of
+ * at most PLD_NOALLOC_MAX_BATCH requests (1 MiB per GPU, held from the
+ * library's load until the process ends). This call never allocates; its
+ * first call on a device looks the array up and clears it (a fill kernel on
+ * `stream`). Every call on a GPU shares that GPU's array, which the kernels
+ * leave cleared after each call: calls that overlap in time on one GPU
+ * (other streams, other host threads) race and must be ordered by the
+ * caller. The tile is chosen as pld_configure's automatic rule does, with the
+ * fused gather.
+ *
+ *  max_len:  bound on every length, 1 <= max_len <= 2^31 - 1 (as in
+ *            pld_create); it sizes the launch.
+ *  batch:    0 <= batch <= PLD_NOALLOC_MAX_BATCH; larger batches are refused.
+ *  out_pos:  device int32[batch] (not NULL).
+ *  out_err:  device uint32 or NULL: bits are OR-ed into it (never cleared
+ *            by the call) when a request's length lies outside [0, max_len]
+ *            or its row pointer is null or misaligned; such requests are
+ *            written as no match. NULL drops the report.
+ *  Other arguments and results exactly as in pld_draft_batch_pos.
+ * Errors: PLD_EINVAL (bad sizes or pointers, batch above the maximum),
+ * PLD_EHIP.
+ */
+#define PLD_NOALLOC_MAX_BATCH 4096
+pld_status pld_draft_batch_noalloc(const int32_t *const *histories, const int32_t *lengths,
+                                   int32_t batch, int64_t max_len, int32_t n_min, int32_t n_max,
+                                   int32_t k_max, int32_t *out_draft, int32_t *out_len,
+                                   int32_t *out_match, int32_t *out_pos, uint32_t *out_err,
+                                   hipStream_t stream);
 
 /*
  * pld_draft_batch for histories laid out at a fixed stride: row b starts at

@@ -29,7 +29,8 @@ PLD_FUSE_MAX_POSITIONS = 64
 # every symbol include/pld.h declares
 EXPORTS = ("pld_create", "pld_create_indexed", "pld_destroy", "pld_configure", "pld_append",
            "pld_histories", "pld_store_reset", "pld_scan_tile", "pld_draft_batch",
-           "pld_draft_batch_pos", "pld_draft_batch_strided", "pld_index_fingerprint_bits",
+           "pld_draft_batch_pos", "pld_draft_batch_noalloc", "pld_draft_batch_strided",
+           "pld_index_fingerprint_bits",
            "pld_draft_store", "pld_append_draft_store",
            "pld_fuse_params_default",
            "pld_fuse", "pld_draft_fuse_batch", "pld_control_params_default", "pld_control",
@@ -98,6 +99,7 @@ def load(path: str = LIB_PATH):
         "pld_store_reset": [vp, vp],
         "pld_draft_batch": [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp],
         "pld_draft_batch_pos": [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp],
+        "pld_draft_batch_noalloc": [vp, vp, i32, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp],
         "pld_draft_batch_strided": [vp, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp,
                                     vp, vp],
         "pld_index_fingerprint_bits": [vp, i32],
@@ -282,6 +284,24 @@ def pld_draft_batch_pos(ctx: int, histories, lengths, batch: int, n_min: int,
         int(k_max), _dev_ptr(out_draft, "out_draft", i32),
         _dev_ptr(out_len, "out_len", i32), _dev_ptr(out_match, "out_match", i32),
         _dev_ptr(out_pos, "out_pos", i32), _stream(stream)))
+
+
+PLD_NOALLOC_MAX_BATCH = 4096
+
+
+def pld_draft_batch_noalloc(histories, lengths, batch: int, max_len: int, n_min: int,
+                            n_max: int, k_max: int, out_draft, out_len, out_match, out_pos,
+                            out_err=None, stream=None) -> None:
+    """pld_draft_batch_pos without a context (nothing allocated); `out_err`
+    is a device uint32 tensor (or None) that error bits are OR-ed into."""
+    import torch
+    i32 = _i32()
+    _check("pld_draft_batch_noalloc", load().pld_draft_batch_noalloc(
+        _dev_ptr(histories, "histories", torch.int64), _dev_ptr(lengths, "lengths", i32),
+        int(batch), int(max_len), int(n_min), int(n_max), int(k_max),
+        _dev_ptr(out_draft, "out_draft", i32), _dev_ptr(out_len, "out_len", i32),
+        _dev_ptr(out_match, "out_match", i32), _dev_ptr(out_pos, "out_pos", i32),
+        _dev_ptr(out_err, "out_err"), _stream(stream)))
 
 
 def pld_draft_batch_strided(ctx: int, base, stride: int, lengths, min_len: int,

@@ -85,16 +85,19 @@ bool valid_tile(int32_t t)
 // batches spread over the whole chip and large ones keep their workgroups
 // few. A request that fits one 4,096-token tile is not split: its single
 // workgroup emits without the cross-workgroup merge.
-static int32_t pick_tile(const pld_ctx *ctx, int32_t batch)
+static int32_t auto_tile(int32_t max_len, int32_t batch)
 {
-    if (ctx->tile_tokens != 0)
-        return ctx->tile_tokens;
-    if (pld::scan_grid(ctx->max_len, 1, 4096) <= 1)
+    if (pld::scan_grid(max_len, 1, 4096) <= 1)
         return 4096;
     for (int32_t t = 4096; t > 1024; t /= 2)
-        if (pld::scan_grid(ctx->max_len, batch, t) >= 1024)
+        if (pld::scan_grid(max_len, batch, t) >= 1024)
             return t;
     return 1024;
+}
+
+static int32_t pick_tile(const pld_ctx *ctx, int32_t batch)
+{
+    return ctx->tile_tokens != 0 ? ctx->tile_tokens : auto_tile(ctx->max_len, batch);
 }
 
 
@@ -836,6 +839,62 @@ pld_status pld_draft_batch_pos(pld_ctx *ctx, const int32_t *const *histories,
         return fail(PLD_EINVAL, "out_pos is null");
     return draft(ctx, histories, nullptr, 0, 0, lengths, batch, n_min, n_max, k_max, out_draft,
                  out_len, out_match, out_pos, stream);
+}
+
+pld_status pld_draft_batch_noalloc(const int32_t *const *histories, const int32_t *lengths,
+                                   int32_t batch, int64_t max_len, int32_t n_min, int32_t n_max,
+                                   int32_t k_max, int32_t *out_draft, int32_t *out_len,
+                                   int32_t *out_match, int32_t *out_pos, uint32_t *out_err,
+                                   hipStream_t stream)
+{
+    if (n_min < 1 || n_max < n_min || n_max > PLD_N_MAX_LIMIT)
+        return fail(PLD_EINVAL, "need 1 <= n_min <= n_max <= %d (got n_min=%d n_max=%d)",
+                    PLD_N_MAX_LIMIT, n_min, n_max);
+    if (k_max < 1)
+        return fail(PLD_EINVAL, "k_max must be >= 1 (got %d)", k_max);
+    if (batch < 0 || batch > pld::kStaticMaxBatch)
+        return fail(PLD_EINVAL, "batch %d outside [0, %d] (the static reduction state's size)",
+                    batch, pld::kStaticMaxBatch);
+    if (max_len < 1 || max_len > 0x7fffffffLL)
+        return fail(PLD_EINVAL, "max_len must be in [1, 2^31-1] (got %lld)", (long long)max_len);
+    if (batch > 0 && (!histories || !lengths || !out_draft || !out_len || !out_match || !out_pos))
+        return fail(PLD_EINVAL, "null buffer pointer");
+    if (batch > 0 && (((uintptr_t)lengths | (uintptr_t)out_draft | (uintptr_t)out_len |
+                       (uintptr_t)out_match | (uintptr_t)out_pos | (uintptr_t)out_err) & 3u))
+        return fail(PLD_EINVAL, "lengths, outputs and out_err must be 4-byte aligned");
+    if ((int64_t)batch * k_max > INT64_MAX / 4)
+        return fail(PLD_EINVAL, "batch * k_max too large");
+    const int32_t ml = (int32_t)max_len;
+    const int32_t tile = auto_tile(ml, batch);
+    if (pld::scan_grid(ml, batch, tile) > 0x7fffffffLL)
+        return fail(PLD_EINVAL, "grid too large: batch %d x tiles for max_len %d", batch, ml);
+    if (batch == 0)
+        return PLD_OK;
+    pld::StaticScratch *sc = nullptr;
+    hipError_t e = pld::static_scratch(&sc, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "static reduction state");
+    pld::DraftArgs a;
+    memset(&a, 0, sizeof(a));
+    a.histories = histories;
+    a.lengths = lengths;
+    a.batch = batch;
+    a.n_min = n_min;
+    a.n_max = n_max;
+    a.k_max = k_max;
+    a.max_len = ml;
+    a.fused = 1;
+    a.out_draft = out_draft;
+    a.out_len = out_len;
+    a.out_match = out_match;
+    a.out_pos = out_pos;
+    a.slots = sc->slots;
+    a.err = out_err ? (unsigned int *)out_err : &sc->err;
+    a.zero16 = &sc->zero16;
+    e = pld::launch_draft(a, tile, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "draft kernel launch");
+    return PLD_OK;
 }
 
 pld_status pld_draft_batch_strided(pld_ctx *ctx, const int32_t *base, int64_t stride,

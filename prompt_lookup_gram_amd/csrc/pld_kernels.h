@@ -155,6 +155,21 @@ struct NgramDraftArgs {
 };
 
 
+// The reduction state of pld_draft_batch_noalloc: the same per-request slots,
+// error word and zero block a context owns, for at most kStaticMaxBatch
+// requests, in a static device array of the library (one per GPU).
+constexpr int32_t kStaticMaxBatch = 4096;
+struct alignas(256) StaticScratch {
+    ReqSlot slots[kStaticMaxBatch];
+    unsigned int err;
+    unsigned int pad[3];
+    int4 zero16;
+};
+
+// The calling device's StaticScratch (its address looked up once per device
+// and the array cleared on `s` the first time), or an error.
+hipError_t static_scratch(StaticScratch **out, hipStream_t s);
+
 // Workgroups the scan launches for a batch (tiles per request x batch).
 int64_t scan_grid(int32_t max_len, int32_t batch, int tile_tokens);
 

@@ -44,6 +44,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "pld_control_step.h"
@@ -1120,6 +1121,48 @@ hipError_t launch_scan(const DraftArgs &a, int64_t tiles_per_req, hipStream_t s)
 }
 
 }  // namespace
+
+}  // namespace pld
+
+// The no-allocation entry point's reduction state: one copy per GPU, held
+// from the moment the library's code object is loaded until the process
+// ends. Host code never names this array's address directly (the name is a
+// host-side stand-in); it uses the device address static_scratch() looks up.
+static __device__ __align__(256) unsigned char scratch[sizeof(pld::StaticScratch)];
+
+namespace pld {
+
+hipError_t static_scratch(StaticScratch **out, hipStream_t s)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *ptr[kMaxDevices];
+    static bool cleared[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        ptr[dev] = p;
+    }
+    if (!cleared[dev]) {
+        // the slots and the zero block must start at zero; a fill kernel
+        // rather than a memset, so that a captured first call replays cleanly
+        e = launch_fill((int32_t *)ptr[dev], (int64_t)(sizeof(StaticScratch) / 4), 0, s);
+        if (e != hipSuccess)
+            return e;
+        cleared[dev] = true;
+    }
+    *out = (StaticScratch *)ptr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_draft(const DraftArgs &a, int tile_tokens, hipStream_t s)
 {

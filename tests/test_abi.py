@@ -191,3 +191,18 @@ def test_create_ngram_rejects_bad_lengths_before_any_hip_call():
     assert _raw("pld_draft_ngram", None, ctypes.byref(p), 1, 16, None, None, None,
                 None) == B.PLD_EINVAL
     assert "ctx is null" in B.pld_last_error()
+
+
+def test_noalloc_rejects_sizes_before_any_hip_call():
+    """The no-allocation entry point refuses a batch above its static
+    reduction state's size and a max_len past the key's position field,
+    on the host, before touching the GPU."""
+    i = ctypes.c_int32
+    for batch, max_len, msg in ((B.PLD_NOALLOC_MAX_BATCH + 1, 100, "batch"),
+                                (4, 2**31, "max_len"), (4, 0, "max_len"), (-1, 100, "batch")):
+        st = _raw("pld_draft_batch_noalloc", None, None, i(batch), ctypes.c_int64(max_len),
+                  i(4), i(12), i(16), None, None, None, None, None, None)
+        assert st == B.PLD_EINVAL
+        assert msg in B.pld_last_error()
+    assert _raw("pld_draft_batch_noalloc", None, None, 0, 100, 4, 12, 16, None, None, None,
+                None, None, None) == B.PLD_OK
