@@ -1023,19 +1023,20 @@ pld_status pld_sync(pld_ctx *ctx, hipStream_t stream)
         e = hipDeviceSynchronize();
     if (e != hipSuccess)
         return hip_fail(e, "pld_sync");
-    if (bits & (pld::kErrLenCapacity | pld::kErrAppendCapacity))
-        return fail(PLD_ECAPACITY, "device reported: %s%s",
-                    (bits & pld::kErrLenCapacity) ? "a history longer than max_len " : "",
-                    (bits & pld::kErrAppendCapacity) ? "an append past max_len" : "");
-    if (bits)
-        return fail(PLD_EINVAL, "device reported: %s%s%s%s%s%s",
-                    (bits & pld::kErrLenNegative) ? "a negative length " : "",
-                    (bits & pld::kErrBadRow) ? "a null or misaligned row pointer " : "",
-                    (bits & pld::kErrAppendNegative) ? "a negative append count " : "",
-                    (bits & pld::kErrBelowMinLen) ? "a length below the promised min_len " : "",
-                    (bits & pld::kErrFuseInput) ? "inconsistent fusion inputs " : "",
-                    (bits & pld::kErrControlInput) ? "a controller outcome out of range" : "");
-    return PLD_OK;
+    if (!bits)
+        return PLD_OK;
+    // every problem read in this call is named; capacity wins the status
+    const pld_status st =
+        (bits & (pld::kErrLenCapacity | pld::kErrAppendCapacity)) ? PLD_ECAPACITY : PLD_EINVAL;
+    return fail(st, "device reported:%s%s%s%s%s%s%s%s",
+                (bits & pld::kErrLenCapacity) ? " a history longer than max_len;" : "",
+                (bits & pld::kErrAppendCapacity) ? " an append past max_len;" : "",
+                (bits & pld::kErrLenNegative) ? " a negative length;" : "",
+                (bits & pld::kErrBadRow) ? " a null or misaligned row pointer;" : "",
+                (bits & pld::kErrAppendNegative) ? " a negative append count;" : "",
+                (bits & pld::kErrBelowMinLen) ? " a length below the promised min_len;" : "",
+                (bits & pld::kErrFuseInput) ? " inconsistent fusion inputs;" : "",
+                (bits & pld::kErrControlInput) ? " a controller outcome out of range;" : "");
 }
 
 const char *pld_strerror(pld_status status)
