@@ -131,15 +131,21 @@ def test_z_crosscheck_config2():
     _check_by_z(w.histories, w.n_min, w.n_max, w.k_max)
 
 
-def test_z_crosscheck_config3_sample():
+def test_z_crosscheck_config3_every_request():
     w = wl.config3()
-    pick = [0, 3, 31, 32, 35, 63]
-    _check_by_z([w.histories[b] for b in pick], w.n_min, w.n_max, w.k_max)
+    assert w.batch == 64
+    _check_by_z(w.histories, w.n_min, w.n_max, w.k_max)
 
 
-def test_z_crosscheck_config4_sample():
+def test_z_crosscheck_config4_every_request():
     w = wl.config4()
-    _check_by_z(w.histories[:2], w.n_min, w.n_max, w.k_max)
+    assert w.batch == 16
+    _check_by_z(w.histories, w.n_min, w.n_max, w.k_max)
+
+
+def test_z_crosscheck_config5_start_every_request():
+    w = wl.config5_start()
+    _check_by_z(w.histories, w.n_min, w.n_max, w.k_max)
 
 
 @pytest.mark.parametrize("seed", range(6))
