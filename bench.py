@@ -5,17 +5,22 @@ kernel) on the 16 x 262,144-token workload (Zipf(1.1) documents with a
 4,096-token copied tail, 0.5% substitutions; n 4..12, k_max 16). Inputs are
 resident in HBM when timing starts.
 
+Steps run from HIP graphs of up to --graph-steps captured calls: exactly
+--warmup untimed steps, then exactly --steps timed steps (n steps are n // G
+replays of a G-step graph and one replay of an (n % G)-step graph). Each
+captured graph is replayed once beforehand and compared with an eager call.
+
 Reported (one JSON line on stdout):
-  value         draft steps/s: wall clock around K steps replayed from HIP
-                graphs of captured calls. Each step reads a different one of
-                R copies of the batch (R * 16.8 MB >= 512 MB), so the 256 MB
-                Infinity Cache cannot serve repeats.
+  value         draft steps/s: host clock around the K timed steps, with a
+                device synchronize on each side. Each step reads a different
+                one of R copies of the batch (R * 16.8 MB >= 512 MB), so the
+                256 MB Infinity Cache cannot serve repeats.
   scan_GBps     4 * sum(L) bytes / the kernel's mean launch time, taken with
-                HIP events around the timed graph replays on the launch
-                stream (one kernel per step).
+                HIP events on the launch stream around the same K steps (one
+                kernel per step).
   roofline      the same against MI355X's 8 TB/s HBM peak; `traffic` is the
                 HBM bytes per launch from the committed rocprofv3 counter
-                summary, used only while the kernel source still matches it.
+                summary, used only while the profiled sources still match it.
   p50_us/p90_us latency of one call: HIP event pair around a single eager
                 call (this includes the event-pair overhead of the runtime);
                 p50_GBps the history bytes over that median.
@@ -45,10 +50,30 @@ METRIC_NGRAM = ("successor-count n-gram draft steps/s (llama.cpp context cache r
                 "batched, exact)")
 METRIC_FUSE = ("lookup draft + draft fusion and long-block scheduling steps/s "
                "(HyperQwen lookup-drafting page, steps 1-3)")
-# counter summaries of pld_scan per lookup workload (default launch)
+# counter summaries of pld_scan per lookup workload (default launch), and of
+# the one-launch lookup + fusion step
 PROFILES = {1: "pld_scan_c1_b1x4096.md", 2: "pld_scan_c2_b8x25000.md",
             3: "pld_scan_c3_b64_ragged.md", 4: "pld_scan_c4_b16x262144.md"}
-KERNEL_SRC = os.path.join(ROOT, "prompt_lookup_gram_amd", "csrc", "pld_kernels.hip")
+PROFILES_FUSE = {4: "pld_scan_fused_c4_b16x262144.md"}
+PROFILE_APPEND_DRAFT = "pld_scan_append_c5_stream_b64.md"
+PROFILE_STREAM = "pld_scan_c5_stream_b64.md"
+# the sources a counter summary is valid for: the kernels and the C-ABI layer
+# that picks their launch (tile, grid)
+CSRC = os.path.join(ROOT, "prompt_lookup_gram_amd", "csrc")
+PROFILED_SOURCES = ("pld_kernels.hip", "pld_kernels.h", "pld_device.h", "pld_api.cpp")
+TIME_SOURCE = ("value, ms_per_step: host clock around the K timed steps, with a device "
+               "synchronize on each side; graph_us_per_step, scan_GBps and roofline: HIP "
+               "events recorded on the launch stream around the same K steps")
+
+
+def source_hash() -> str:
+    """First 16 hex digits of the SHA-256 of the profiled sources, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in PROFILED_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def calibration_copies(torch, dev):
@@ -61,24 +86,89 @@ def calibration_copies(torch, dev):
     torch.cuda.synchronize()
 
 
-def profiled_traffic(config: int = 4):
-    """HBM bytes per launch from the workload's committed counter summary,
-    if it was taken on the kernel source as it is now (else None)."""
-    import hashlib
-    if config not in PROFILES:
+def profiled_traffic(name, key="traffic-bytes-per-launch"):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the sources as they are now (else None). The default key is the
+    FETCH_SIZE + WRITE_SIZE figure scaled by a plain copy's reading;
+    "traffic-sized-bytes-per-launch" counts the read requests by size."""
+    if name is None:
         return None
     try:
-        text = open(os.path.join(ROOT, "profiles", PROFILES[config])).read()
-        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+        text = open(os.path.join(ROOT, "profiles", name)).read()
+        src = source_hash()
     except OSError:
         return None
     sha = traffic = None
     for line in text.splitlines():
-        if line.startswith("kernel-source-sha256-16:"):
+        if line.startswith("source-sha256-16:"):
             sha = line.split(":", 1)[1].strip()
-        if line.startswith("traffic-bytes-per-launch:"):
+        if line.startswith(key + ":"):
             traffic = int(line.split(":", 1)[1].strip())
     return traffic if sha == src else None
+
+
+TRAFFIC_NOTE = ("traffic: FETCH_SIZE and WRITE_SIZE per launch, each scaled by its reading "
+                "for a 64 MiB copy; traffic_by_request_size: the L2's 128-, 64- and 32-byte "
+                "read requests counted at their sizes, plus WRITE_SIZE (both from the "
+                "committed counter summary of this workload, used while the profiled "
+                "sources match it)")
+
+
+def step_plan(n: int, g: int) -> list:
+    """Graph sizes whose replays run exactly n steps: n // g replays of a
+    g-step graph, then one replay of an (n % g)-step graph."""
+    q, r = divmod(max(0, int(n)), int(g))
+    return [g] * q + ([r] if r else [])
+
+
+class GraphSteps:
+    """Steps replayed from HIP graphs captured on a side stream. capture(m)
+    records steps 0..m-1; it is called once for each graph size in use."""
+
+    def __init__(self, torch, capture, g):
+        self.torch, self.capture, self.g = torch, capture, int(g)
+        self.graphs = {}
+        self.stream = torch.cuda.Stream()
+
+    def prepare(self, *counts):
+        """Capture every graph that running each of `counts` steps needs;
+        returns the captured sizes."""
+        torch = self.torch
+        for n in counts:
+            for m in step_plan(n, self.g):
+                if m not in self.graphs:
+                    graph = torch.cuda.CUDAGraph()
+                    torch.cuda.synchronize()
+                    with torch.cuda.graph(graph, stream=self.stream):
+                        self.capture(m)
+                    torch.cuda.synchronize()
+                    self.graphs[m] = graph
+        return sorted(self.graphs)
+
+    def run(self, n):
+        for m in step_plan(n, self.g):
+            self.graphs[m].replay()
+
+    def last(self, n):
+        """Size of the graph that runs the last of n steps."""
+        plan = step_plan(n, self.g)
+        return plan[-1] if plan else 0
+
+
+def timed_steps(torch, gs, k):
+    """Exactly k steps between two device synchronizes: (host seconds, HIP
+    event seconds on the current stream, where the graphs are launched)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    gs.run(k)
+    e1.record()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, e0.elapsed_time(e1) * 1e-3
+
+
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
 
@@ -134,6 +224,9 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with 8 plain 64 MiB device copies (a counter "
                          "reference of known size for rocprofv3 --pmc)")
+    ap.add_argument("--print-source-hash", action="store_true",
+                    help="print the hash a counter summary under profiles/ records for "
+                         "the kernel sources, and exit")
     return ap.parse_args()
 
 
@@ -149,6 +242,12 @@ def cpu_model() -> str:
 
 def main():
     args = parse()
+    if args.print_source_hash:
+        print(source_hash())
+        return
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be at least 1 and --warmup at least 0", file=sys.stderr)
+        sys.exit(2)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: requests shard across GPUs with "
@@ -212,44 +311,33 @@ def main():
             B.pld_draft_batch(ctx, rows_all[r], copies[r].lengths, w.batch, w.n_min,
                               w.n_max, w.k_max, out[0], out[1], out[2], stream=stream)
     B.pld_configure(ctx, args.tile, args.fused)
+    tile = B.pld_scan_tile(ctx, w.batch)   # the tile the library launches
 
     # reference output (eager) for the graph check and the parity check
     call(0)
     assert B.pld_sync(ctx) == B.PLD_OK
     eager = [t.clone() for t in out[:3]]
 
-    # ---- HIP graph of G consecutive steps (rotating copies) -----------------
+    # ---- HIP graphs of consecutive steps (rotating copies) ------------------
     G = max(1, min(args.graph_steps, args.steps))
-    cap_stream = torch.cuda.Stream()
-    graph = torch.cuda.CUDAGraph()
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph, stream=cap_stream):
-        for i in range(G):
-            call(i)
-    torch.cuda.synchronize()
-    for _ in range(3):  # every replay must reproduce the eager result
+    gs = GraphSteps(torch, lambda m: [call(i) for i in range(m)], G)
+
+    def check_out(what):
+        for a_, b_ in zip(eager, out[:3]):
+            assert torch.equal(a_, b_), f"{what} differs from the eager call"
+
+    graph_sizes = gs.prepare(args.steps, args.warmup)
+    for m in graph_sizes:  # each captured graph reproduces the eager result
         for t in out[:3]:
             t.fill_(-9)
-        graph.replay()
+        gs.graphs[m].replay()
         torch.cuda.synchronize()
-        for a, b_ in zip(eager, out[:3]):
-            assert torch.equal(a, b_), "graph replay differs from eager call"
-
-    reps_w = max(1, args.warmup // G)
-    reps = max(1, -(-args.steps // G))
-    steps = reps * G
-    for _ in range(reps_w):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(reps):
-        graph.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
+        check_out(f"a replay of the {m}-step graph")
+    gs.run(args.warmup)                     # exactly W untimed steps
+    wall_s, gpu_s = timed_steps(torch, gs, args.steps)   # exactly K timed steps
+    check_out("the last timed step")
+    steps = args.steps
+    gpu_ms = gpu_s * 1e3
     ms_per_step = wall_s * 1e3 / steps
     steps_per_s = steps / wall_s
 
@@ -273,19 +361,20 @@ def main():
     warm = None
     if args.warm:
         g2 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g2, stream=cap_stream):
+        with torch.cuda.graph(g2, stream=gs.stream):
             for i in range(G):
                 call(0)
         torch.cuda.synchronize()
         g2.replay()
         torch.cuda.synchronize()
+        reps = max(1, steps // G)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
             g2.replay()
         e1.record()
         torch.cuda.synchronize()
-        warm_us = e0.elapsed_time(e1) * 1e3 / steps
+        warm_us = e0.elapsed_time(e1) * 1e3 / (reps * G)
         warm = {"us_per_step": warm_us, "GBps": bytes_step / warm_us / 1e3,
                 "note": "same copy every step (Infinity-Cache resident)"}
 
@@ -296,19 +385,20 @@ def main():
                                          [c.flat for c in copies])]
         red = torch.empty((), dtype=torch.int32, device=dev)
         g3 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g3, stream=cap_stream):
+        with torch.cuda.graph(g3, stream=gs.stream):
             for i in range(G):
                 torch.amax(flat[i % rot], 0, out=red)
         torch.cuda.synchronize()
         g3.replay()
         torch.cuda.synchronize()
+        reps = max(1, steps // G)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
             g3.replay()
         e1.record()
         torch.cuda.synchronize()
-        lib_us = e0.elapsed_time(e1) * 1e3 / steps
+        lib_us = e0.elapsed_time(e1) * 1e3 / (reps * G)
         library = {"op": "torch.amax over the same rotated copies", "us_per_launch": lib_us,
                    "GBps": flat[0].numel() * 4 / lib_us / 1e3}
 
@@ -321,34 +411,33 @@ def main():
 
     graph_us = gpu_ms * 1e3 / steps           # mean launch time (one kernel per step)
     scan_gbps = bytes_step / (graph_us * 1e-6) / 1e9
-    # the library's automatic tile (tile 0): 4,096 when a request fits one
-    # such tile, else the largest of 4,096, 2,048 and 1,024 that gives the
-    # scan at least 1,024 workgroups
-    max_len = max(1, int(w.lengths.max()))
-    auto = 4096 if max_len - 1 <= 4096 else next(
-        (t for t in (4096, 2048) if w.batch * -(-(max_len - 1) // t) >= 1024), 1024)
-    default_launch = (args.tile in (0, auto) and args.fused in (-1, 1)
+    default_launch = (args.tile in (0, tile) and args.fused in (-1, 1)
                       and args.layout == "rows")
-    traffic = profiled_traffic(args.config) if default_launch else None
+    prof = PROFILES.get(args.config) if default_launch else None
+    traffic, traffic_sized = (profiled_traffic(prof),
+                              profiled_traffic(prof, "traffic-sized-bytes-per-launch"))
     rec = {
         "metric": METRIC,
         "value": round(steps_per_s, 1),
         "unit": "draft steps/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": reps_w * G,
+        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int32",
         "data": "synthetic",
+        "time_source": TIME_SOURCE,
         "config": {"workload": w.name, "batch": w.batch, "layout": args.layout,
-                   "tile_tokens": args.tile or auto,
+                   "tile_tokens": tile,
                    "history_tokens": int(w.lengths.max()),
                    "n_min": w.n_min, "n_max": w.n_max, "k_max": w.k_max,
                    "bytes_per_step": bytes_step, "rotated_copies": rot,
-                   "graph_steps": G},
+                   "graph_steps": G, "graph_sizes": graph_sizes},
+        "capture_check": "each captured graph replayed once before the warm-up and "
+                         "compared with an eager call; the last timed step compared too",
         "request_drafts_per_s": round(steps_per_s * w.batch, 1),
         "scan_GBps": round(scan_gbps, 1),
         "hbm_frac": round(scan_gbps / HBM_PEAK_GBPS, 4),
@@ -361,9 +450,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(scan_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(scan_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "traffic_by_request_size": traffic_sized, "traffic_note": TRAFFIC_NOTE,
                      "kernel": "pld_scan",
-                     "time_source": "HIP events around the timed graph replays "
-                                    f"({steps} launches, rotated copies)"},
+                     "time_source": "HIP events on the launch stream around the K "
+                                    f"timed steps ({steps} launches, rotated copies)"},
     }
     if warm:
         rec["warm"] = warm
@@ -441,6 +531,11 @@ def bench_fuse(args, torch, B, wl, dev, w):
     rows_all = _t.stack([c.rows for c in copies]).contiguous()
     ctx = B.pld_create(w.batch, base.max_len)
     B.pld_configure(ctx, args.tile, args.fused)
+    tile = B.pld_scan_tile(ctx, w.batch)
+    default_launch = args.tile in (0, tile) and args.fused in (-1, 1) and args.fuse == "one"
+    prof = PROFILES_FUSE.get(args.config) if default_launch else None
+    traffic, traffic_sized = (profiled_traffic(prof),
+                              profiled_traffic(prof, "traffic-sized-bytes-per-launch"))
     out = B.alloc_outputs(w.batch, k, device=dev)
     state = _t.zeros((w.batch, B.PLD_FUSE_STATE_WORDS), dtype=_t.int32, device=dev)
     blk = _t.empty((w.batch, n_pos), dtype=_t.int32, device=dev)
@@ -479,37 +574,32 @@ def bench_fuse(args, torch, B, wl, dev, w):
     long_frac = float(np.mean([t[6][:, 0] for t in trace]))
     mean_pos = float(np.mean([t[4] for t in trace]))
 
-    cap_stream = _t.cuda.Stream()
-    graph = _t.cuda.CUDAGraph()
-    _t.cuda.synchronize()
-    with _t.cuda.graph(graph, stream=cap_stream):
+    def capture(m):  # schedule state zeroed, then steps 0..m-1 of the eager pass
         state.zero_()
-        for i in range(G):
+        for i in range(m):
             call(i)
-    _t.cuda.synchronize()
-    for _ in range(3):  # every replay reproduces the eager pass's last step
+
+    gs = GraphSteps(_t, capture, G)
+
+    def check_step(m, what):  # the state after m steps from zero
+        assert np.array_equal(blk.cpu().numpy(), trace[m - 1][3]), what
+        assert np.array_equal(state.cpu().numpy(), trace[m - 1][6]), what
+
+    graph_sizes = gs.prepare(args.steps, args.warmup)
+    for m in graph_sizes:  # each captured graph reproduces the eager pass
         blk.fill_(-9)
-        graph.replay()
+        gs.graphs[m].replay()
         _t.cuda.synchronize()
-        assert np.array_equal(blk.cpu().numpy(), trace[-1][3]), "graph replay differs"
-        assert np.array_equal(state.cpu().numpy(), trace[-1][6]), "graph replay differs"
-    reps_w = max(1, args.warmup // G)
-    reps = max(1, -(-args.steps // G))
-    steps = reps * G
-    for _ in range(reps_w):
-        graph.replay()
-    _t.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0, ev1 = _t.cuda.Event(enable_timing=True), _t.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(reps):
-        graph.replay()
-    ev1.record()
-    _t.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
-    gpu_us = ev0.elapsed_time(ev1) * 1e3 / steps
+        check_step(m, f"a replay of the {m}-step graph differs from the eager pass")
+    gs.run(args.warmup)
+    wall_s, gpu_s = timed_steps(_t, gs, args.steps)
+    check_step(gs.last(args.steps), "the last timed step differs from the eager pass")
+    steps = args.steps
+    gpu_us = gpu_s * 1e6 / steps
     assert B.pld_sync(ctx) == B.PLD_OK
     B.pld_destroy(ctx)
+    if args.calibrate_copy:
+        calibration_copies(_t, dev)
     scan_gbps = bytes_step / (gpu_us * 1e-6) / 1e9
     launches = 1 if args.fuse == "one" else 2
     rec = {
@@ -518,31 +608,42 @@ def bench_fuse(args, torch, B, wl, dev, w):
         "unit": "draft+fuse steps/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": reps_w * G,
+        "warmup": args.warmup,
         "ms_per_step": round(wall_s * 1e3 / steps, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int32",
         "data": "synthetic",
+        "time_source": TIME_SOURCE,
         "config": {"workload": w.name, "batch": w.batch, "layout": "rows",
                    "history_tokens": int(w.lengths.max()), "n_min": w.n_min,
                    "n_max": w.n_max, "k_max": k, "bytes_per_step": bytes_step,
-                   "rotated_copies": rot, "graph_steps": G,
+                   "rotated_copies": rot, "graph_steps": G, "graph_sizes": graph_sizes,
+                   "tile_tokens": tile,
                    "fuse": {f: getattr(params, f) for f, _ in params._fields_},
                    "launches_per_step": launches},
+        "capture_check": "each captured graph (schedule state zeroed first) replayed once "
+                         "before the warm-up and compared with the eager pass; the last "
+                         "timed step compared too",
         "graph_us_per_step": round(gpu_us, 3),
         "scan_GBps": round(scan_gbps, 1),
         "hbm_frac": round(scan_gbps / HBM_PEAK_GBPS, 4),
         "long_block_step_frac": round(long_frac, 4),
         "mean_draft_positions": round(mean_pos, 3),
+        # one launch per step: the step's time is the kernel's own; two: the
+        # whole step, a lower bound of the scan kernel's fraction
         "roofline": {"bound": "hbm", "achieved": round(scan_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(scan_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "kernel": "pld_scan" + (" + pld_fuse_kernel"
-                                                              if launches == 2 else ""),
-                     "time_source": f"HIP events around the timed graph replays ({steps} "
-                                    f"steps, {launches} launch(es) each, state zeroed "
-                                    f"once per {G} steps)"},
+                     "traffic": traffic, "traffic_by_request_size": traffic_sized,
+                     "traffic_note": TRAFFIC_NOTE,
+                     "kernel": ("pld_scan (lookup, fusion and schedule in one launch)"
+                                if launches == 1 else "pld_scan + pld_fuse_kernel (whole step)"),
+                     "bytes": "history bytes per step (the fusion's per-request inputs and "
+                              "outputs, under 200 bytes a request, are not counted)",
+                     "time_source": f"HIP events on the launch stream around the K timed "
+                                    f"steps ({steps} steps, {launches} launch(es) each, "
+                                    f"state zeroed once per graph replay)"},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -603,49 +704,51 @@ def bench_ngram(args, torch, B, wl, dev, w):
     assert B.pld_sync(ctx) == B.PLD_OK
     ref = (out_d.cpu().numpy(), out_l.cpu().numpy(), out_v.cpu().numpy())
 
-    cap_stream = torch.cuda.Stream()
-    graph = torch.cuda.CUDAGraph()
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph, stream=cap_stream):
-        for _ in range(G):
+    def capture(m):
+        for _ in range(m):
             B.pld_draft_ngram(ctx, params, nb, k, out_d, out_l, out_v)
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    assert np.array_equal(out_d.cpu().numpy(), ref[0]), "graph replay differs"
-    reps_w = max(1, args.warmup // G)
-    reps = max(1, -(-args.steps // G))
-    steps = reps * G
-    for _ in range(reps_w):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(reps):
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
-    gpu_us = e0.elapsed_time(e1) * 1e3 / steps
+
+    gs = GraphSteps(torch, capture, G)
+
+    def check_out(what):
+        assert (np.array_equal(out_d.cpu().numpy(), ref[0])
+                and np.array_equal(out_l.cpu().numpy(), ref[1])
+                and np.array_equal(out_v.cpu().numpy(), ref[2])), what
+
+    graph_sizes = gs.prepare(args.steps, args.warmup)
+    for m in graph_sizes:
+        out_d.fill_(-9)
+        gs.graphs[m].replay()
+        torch.cuda.synchronize()
+        check_out(f"a replay of the {m}-step graph differs from the eager call")
+    gs.run(args.warmup)
+    wall_s, gpu_s = timed_steps(torch, gs, args.steps)
+    check_out("the last timed step differs from the eager call")
+    steps = args.steps
+    gpu_us = gpu_s * 1e6 / steps
     assert B.pld_sync(ctx) == B.PLD_OK
     B.pld_destroy(ctx)
+    if args.calibrate_copy:
+        calibration_copies(torch, dev)
     rec = {
         "metric": METRIC_NGRAM,
         "value": round(steps / wall_s, 1),
         "unit": "draft steps/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": reps_w * G,
+        "warmup": args.warmup,
         "ms_per_step": round(wall_s * 1e3 / steps, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int32",
         "data": "synthetic",
+        "time_source": TIME_SOURCE.replace("scan_GBps and roofline", "ns_per_drafted_token"),
         "config": {"workload": w.name, "batch": nb, "history_tokens": max_len,
                    "n_min": params.n_min, "n_max": params.n_max, "k_max": k,
                    "min_count": list(params.min_count),
-                   "min_percent": list(params.min_percent), "graph_steps": G},
+                   "min_percent": list(params.min_percent), "graph_steps": G,
+                   "graph_sizes": graph_sizes},
         "graph_us_per_step": round(gpu_us, 3),
         "mean_draft_tokens": round(float(ref[1].mean()), 3),
         "drafted_tokens_per_step": int(ref[1].sum()),
@@ -679,13 +782,47 @@ def bench_stream(args, torch, B, wl, dev):
     """The streaming decode: 64 requests from 32,768 tokens, 1,024 steps of
     pld_draft_batch on the context's own store, then pld_append of the 1..16
     tokens each request accepted. The appended tokens follow each request's
-    previous draft while it lasts, then fresh Zipf tokens; they are fixed
-    by one untimed closed-loop pass, then all 1,024 steps are captured in a
-    HIP graph and replayed from the same start state."""
+    previous draft while it lasts, then fresh Zipf tokens.
+
+    The oracle runs first, over all 1,024 steps (the CPU baseline leg): its
+    drafts fix the append stream, and every GPU step is compared with it.
+    With --no-cpu-baseline the GPU's own drafts fix the stream instead. One
+    untimed eager pass on the GPU follows that stream; then all 1,024 steps
+    are captured in a HIP graph and replayed from the same start state."""
     start_len = args.stream_start or wl.STREAM_START_LEN
     start = wl.config5_start(start_len)
     nb, steps_n, width = start.batch, wl.STREAM_STEPS, wl.STREAM_MAX_APPEND
     max_len = start_len + steps_n * width
+    toks = np.zeros((steps_n, nb, width), np.int32)
+    cnts = np.zeros((steps_n, nb), np.int32)
+
+    # ---- the oracle's closed loop (CPU baseline leg) -------------------------
+    want, cpu = None, None
+    if not args.no_cpu_baseline:
+        import oracle
+        hs = [h.copy() for h in start.histories]
+        op = oracle.NgramParams()
+        want, cpu_s = [], 0.0
+        for step in range(steps_n):
+            t_ = time.perf_counter()
+            if args.ngram:
+                od, ol, om = oracle.ngram_draft(op, hs, start.k_max)
+            else:
+                od, ol, om, _ = oracle.draft(hs, start.n_min, start.n_max, start.k_max)
+            cpu_s += time.perf_counter() - t_
+            want.append((od, ol, om))
+            counts, fresh = wl.stream_step_draws(step)
+            toks[step] = wl.compose_append(od, ol, counts, fresh)
+            cnts[step] = counts
+            t_ = time.perf_counter()
+            hs = oracle.append(hs, toks[step], cnts[step])
+            cpu_s += time.perf_counter() - t_
+        cpu = {"value": round(steps_n / cpu_s, 3), "unit": "draft steps/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"all {steps_n} streaming steps (draft + append, "
+                         f"{'successor-count' if args.ngram else 'lookup'} oracle, "
+                         f"{cpu_s:.1f} s, one thread, {cpu_model()})"}
+
     if args.index:
         ctx = B.pld_create_indexed(nb, max_len, start.n_min, start.n_max)
     elif args.ngram:
@@ -729,23 +866,26 @@ def bench_stream(args, torch, B, wl, dev):
         B.pld_store_reset(ctx)
         B.pld_append(ctx, init, start_len, init_counts, nb)
 
-    # untimed closed loop: fixes the append stream from the GPU's drafts
+    # ---- untimed eager pass: every step's drafts, on the fixed stream -------
     restart()
-    toks = np.zeros((steps_n, nb, width), np.int32)
-    cnts = np.zeros((steps_n, nb), np.int32)
-    first_drafts = []  # every step's drafts, for the oracle comparison
     lengths = np.full(nb, start_len, np.int64)
     total_tokens = 0
+    mismatch, mean_len = None, []
     for step in range(steps_n):
         draft()
         d, l = out[0].cpu().numpy(), out[1].cpu().numpy()
-        first_drafts.append((d.copy(), l.copy(),
-                             (levels if args.ngram else out[2]).cpu().numpy()))
+        m = (levels if args.ngram else out[2]).cpu().numpy()
+        mean_len.append(float(l.mean()))
+        if want is None:
+            counts, fresh = wl.stream_step_draws(step)
+            toks[step] = wl.compose_append(d, l, counts, fresh)
+            cnts[step] = counts
+        elif mismatch is None and not (np.array_equal(d, want[step][0])
+                                       and np.array_equal(l, want[step][1])
+                                       and np.array_equal(m, want[step][2])):
+            mismatch = step
         total_tokens += int(lengths.sum())
-        counts, fresh = wl.stream_step_draws(step)
-        toks[step] = wl.compose_append(d, l, counts, fresh)
-        cnts[step] = counts
-        lengths += counts
+        lengths += cnts[step]
         B.pld_append(ctx, torch.from_numpy(toks[step]).to(dev), width,
                      torch.from_numpy(cnts[step]).to(dev), nb)
     assert B.pld_sync(ctx) == B.PLD_OK
@@ -753,7 +893,7 @@ def bench_stream(args, torch, B, wl, dev):
     toks_d = torch.from_numpy(toks).to(dev)
     cnts_d = torch.from_numpy(cnts).to(dev)
 
-    # one graph holds all 1,024 steps, in the closed loop's order: draft,
+    # one graph holds all 1,024 steps, in the eager pass's order: draft,
     # then append the tokens that step accepted
     cap = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
@@ -779,9 +919,13 @@ def bench_stream(args, torch, B, wl, dev):
                 draft()
                 control()
                 B.pld_append(ctx, toks_d[step], width, cnts_d[step], nb)
+
+    # whole replays of the 1,024-step graph: enough to cover the requested
+    # warm-up and timed steps
+    warm_reps = -(-args.warmup // steps_n)
+    reps = max(1, -(-args.steps // steps_n))
     times = []
-    reps = max(1, args.steps // steps_n) if args.steps >= steps_n else 1
-    for rep in range(reps + 1):  # the first replay is warm-up
+    for rep in range(warm_reps + reps):
         restart()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -793,8 +937,8 @@ def bench_stream(args, torch, B, wl, dev):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         for a_, b_ in zip(final_ref, out[:3]):
-            assert torch.equal(a_, b_), "graph replay differs from the closed-loop pass"
-        if rep:
+            assert torch.equal(a_, b_), "graph replay differs from the eager pass"
+        if rep >= warm_reps:
             times.append((wall, e0.elapsed_time(e1) * 1e-3))
     assert B.pld_sync(ctx) == B.PLD_OK
     B.pld_destroy(ctx)
@@ -809,13 +953,17 @@ def bench_stream(args, torch, B, wl, dev):
         "unit": "draft steps/s",
         "n_gpus": 1,
         "steps": steps_n * len(times),
-        "warmup": steps_n,
+        "warmup": steps_n * warm_reps,
         "ms_per_step": round(wall * 1e3 / steps_n, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int32",
         "data": "synthetic",
+        "time_source": ("value, ms_per_step: host clock around one replay of the 1,024-step "
+                        "graph (median over the timed replays), with a device synchronize on "
+                        "each side; us_per_step_append_plus_draft and roofline: HIP events "
+                        "on the launch stream around the same replays"),
         "config": {"workload": start.name, "batch": nb, "start_tokens": start_len,
                    "steps": steps_n, "n_min": start.n_min, "n_max": start.n_max,
                    "k_max": start.k_max, "mean_bytes_per_step": round(bytes_mean),
@@ -824,7 +972,9 @@ def bench_stream(args, torch, B, wl, dev):
                    "calls_per_step": ((1 if args.append_draft else 2)
                                       + int(args.control and not args.control_fused)),
                    "controller": ("in the draft's launch" if args.control_fused else
-                                  "own launch" if args.control else None)},
+                                  "own launch" if args.control else None),
+                   "append_stream": ("the oracle's drafts" if want is not None
+                                     else "the GPU's own drafts (no oracle run)")},
         "us_per_step_append_plus_draft": round(gpu_s * 1e6 / steps_n, 3),
         # for the index: the history bytes a scan would have read, per second
         ("scan_equivalent_GBps" if args.index else "scan_GBps"):
@@ -832,47 +982,40 @@ def bench_stream(args, torch, B, wl, dev):
         "hbm_frac": None if (args.index or args.ngram) else
             round(bytes_mean * steps_n / gpu_s / 1e9 / HBM_PEAK_GBPS, 4),
     }
+    if args.steps % steps_n or args.warmup % steps_n:
+        rec["steps_requested"], rec["warmup_requested"] = args.steps, args.warmup
     if not (args.index or args.ngram):
-        # the whole step (the append and the scan, one or two launches) against
-        # the HBM peak: a lower bound of the scan kernel's own fraction
+        one_launch = args.append_draft and not (args.control and not args.control_fused)
+        plain = not args.control and start_len == wl.STREAM_START_LEN
+        prof = (PROFILE_APPEND_DRAFT if one_launch else PROFILE_STREAM) if plain else None
         kernels = (["pld_scan"] + ([] if args.append_draft else ["pld_append_kernel"])
                    + (["pld_control_kernel"] if args.control and not args.control_fused else []))
         rec["roofline"] = {
             "bound": "hbm", "achieved": rec["scan_GBps"], "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": rec["hbm_frac"], "traffic": None,
-            "kernel": " + ".join(kernels),
-            "time_source": f"HIP events around the replayed {steps_n}-step graph, whole step "
-                           f"({len(kernels)} launch{'es' if len(kernels) > 1 else ''}); "
+            "unit": "GB/s", "frac": rec["hbm_frac"],
+            "traffic": profiled_traffic(prof),
+            "traffic_by_request_size": profiled_traffic(prof, "traffic-sized-bytes-per-launch"),
+            "traffic_note": TRAFFIC_NOTE + "; the median dispatch of the 1,024 steps, whose "
+                            "history bytes grow step by step",
+            "kernel": (" + ".join(kernels) + (" (the append in the scan's launch: one "
+                                              "launch per step)" if one_launch else
+                                              " (whole step)")),
+            "time_source": f"HIP events around the replayed {steps_n}-step graph "
+                           f"({len(kernels)} launch{'es' if len(kernels) > 1 else ''} a step"
+                           f"{', plus the last append' if args.append_draft else ''}); "
                            "bytes = the mean history bytes per step"}
     if args.ngram:
         # a different drafter: no history bytes are read per step
         rec["metric"] = METRIC_NGRAM
         del rec["scan_GBps"]
         rec["config"]["n_min"], rec["config"]["n_max"] = nparams.n_min, nparams.n_max
-        rec["mean_draft_tokens"] = round(float(np.mean([f[1] for f in first_drafts])), 3)
-    if not args.no_cpu_baseline:
-        import oracle
-        hs = [h.copy() for h in start.histories]
-        n, parity, t_start = 0, True, time.perf_counter()
-        op = oracle.NgramParams()
-        while n < steps_n and time.perf_counter() - t_start < args.cpu_seconds:
-            if args.ngram:
-                od, ol, om = oracle.ngram_draft(op, hs, start.k_max)
-            else:
-                od, ol, om, _ = oracle.draft(hs, start.n_min, start.n_max, start.k_max)
-            gd, gl, gm = first_drafts[n]
-            parity &= (np.array_equal(od, gd) and np.array_equal(ol, gl)
-                       and np.array_equal(om, gm))
-            hs = oracle.append(hs, toks[n], cnts[n])
-            n += 1
-        el = time.perf_counter() - t_start
-        rec["cpu_baseline"] = {
-            "value": round(n / el, 3), "unit": "draft steps/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"the first {n} streaming steps (append + draft, {el:.1f} s, "
-                      f"one thread, {cpu_model()})"}
-        rec["parity"] = "bit-exact" if parity else "MISMATCH"
-        if not parity:
+        rec["mean_draft_tokens"] = round(float(np.mean(mean_len)), 3)
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
+        rec["parity"] = ("bit-exact" if mismatch is None else "MISMATCH")
+        rec["parity_steps"] = (f"all {steps_n} steps" if mismatch is None
+                               else f"first mismatch at step {mismatch}")
+        if mismatch is not None:
             print(json.dumps(rec))
             sys.exit(1)
     print(json.dumps(rec), flush=True)
