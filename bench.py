@@ -830,6 +830,7 @@ def bench_stream(args, torch, B, wl, dev):
     else:
         ctx = B.pld_create(nb, max_len, own_store=True)
     rows, lens = B.pld_histories(ctx)
+    tile = None if (args.index or args.ngram) else B.pld_scan_tile(ctx, nb)
     # controller inputs: every outcome "0 accepted in time 1.0" is valid for
     # any previous choice, so the captured steps need no host round trip
     cparams = B.pld_control_params_default()
@@ -973,6 +974,7 @@ def bench_stream(args, torch, B, wl, dev):
                                       + int(args.control and not args.control_fused)),
                    "controller": ("in the draft's launch" if args.control_fused else
                                   "own launch" if args.control else None),
+                   "tile_tokens": tile,
                    "append_stream": ("the oracle's drafts" if want is not None
                                      else "the GPU's own drafts (no oracle run)")},
         "us_per_step_append_plus_draft": round(gpu_s * 1e6 / steps_n, 3),
