@@ -188,7 +188,7 @@ def parse():
                          "history)")
     ap.add_argument("--graph-steps", type=int, default=128,
                     help="draft calls captured per HIP graph")
-    ap.add_argument("--latency-calls", type=int, default=2000)
+    ap.add_argument("--latency-calls", type=int, default=200)
     ap.add_argument("--tile", type=int, default=0, help="0 = library default")
     ap.add_argument("--fused", type=int, default=-1, help="-1 = library default")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

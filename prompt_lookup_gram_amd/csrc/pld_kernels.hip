@@ -28,8 +28,9 @@
 //      history's last token (about 2-4% on Zipf text) and, when n_min >= 3,
 //      its two predecessors hold the two tokens before that (the tokens
 //      before a chunk come from the neighbouring lane by a DPP wavefront
-//      shift); survivors extend backwards from LDS up to m tokens, several
-//      tokens per LDS round trip.
+//      shift; two of the three tokens are compared as one 64-bit pair);
+//      survivors extend backwards from LDS up to m tokens, several tokens
+//      per LDS round trip.
 //   4. Per-thread max -> wavefront max (DPP row shifts and broadcasts on
 //      2x32-bit halves), only in wavefronts that found a match, then either
 //      a 64-bit atomicMax into the request's slot per wavefront (separate
@@ -701,24 +702,32 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
     const int32_t span_end = rq0 + 4 * (kHaloChunks + kSpan);
     const int32_t hi = last_wave ? nrel : (span_end < nrel ? span_end : nrel);
     const int32_t ell0 = FILTER3 ? 3 : 1;  // tokens known to match for a survivor
+    // two adjacent suffix tokens as one 64-bit value (earlier token low)
+    const u64 q21 = (u64)(uint32_t)p2 | (u64)(uint32_t)p1 << 32;
+    const u64 q32 = (u64)(uint32_t)p3 | (u64)(uint32_t)p2 << 32;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
         const int32_t r0 = rq0 + 4 * (kHaloChunks + k * kWave + lane);  // rel of token 0
         bool c[4];
         if constexpr (FILTER3) {
-            // the two tokens before this chunk
-            int32_t pz = __builtin_amdgcn_mov_dpp(v[k].z, 0x138 /* wave_shr:1 */, 0xf, 0xf, true);
-            int32_t pw = __builtin_amdgcn_mov_dpp(v[k].w, 0x138 /* wave_shr:1 */, 0xf, 0xf, true);
-            const int32_t lz = k > 0 ? __builtin_amdgcn_readlane(v[k - 1].z, kWave - 1)
+            // the two tokens before this chunk: lane l - 1's last two, by a
+            // wavefront shift; lane 0, which has no source lane and keeps
+            // the shift's `old` operand, gets lane 63 of the previous slot
+            // (rotated to lane 0) or the halo's last chunk
+            const int32_t oz = k > 0 ? __builtin_amdgcn_mov_dpp(v[k - 1].z, 0x13c /* wave_ror:1 */, 0xf, 0xf, false)
                                      : __builtin_amdgcn_readlane(v[kPer].z, kHaloChunks - 1);
-            const int32_t lw = k > 0 ? __builtin_amdgcn_readlane(v[k - 1].w, kWave - 1)
+            const int32_t ow = k > 0 ? __builtin_amdgcn_mov_dpp(v[k - 1].w, 0x13c /* wave_ror:1 */, 0xf, 0xf, false)
                                      : __builtin_amdgcn_readlane(v[kPer].w, kHaloChunks - 1);
-            pz = lane == 0 ? lz : pz;
-            pw = lane == 0 ? lw : pw;
-            c[0] = v[k].x == p1 && pw == p2 && pz == p3;
-            c[1] = v[k].y == p1 && v[k].x == p2 && pw == p3;
-            c[2] = v[k].z == p1 && v[k].y == p2 && v[k].x == p3;
-            c[3] = v[k].w == p1 && v[k].z == p2 && v[k].y == p3;
+            const int32_t pz = __builtin_amdgcn_update_dpp(oz, v[k].z, 0x138 /* wave_shr:1 */, 0xf, 0xf, false);
+            const int32_t pw = __builtin_amdgcn_update_dpp(ow, v[k].w, 0x138 /* wave_shr:1 */, 0xf, 0xf, false);
+            // each position's three tokens as a 64-bit pair and one token
+            const u64 xy = (u64)(uint32_t)v[k].x | (u64)(uint32_t)v[k].y << 32;
+            const u64 zw = (u64)(uint32_t)v[k].z | (u64)(uint32_t)v[k].w << 32;
+            const u64 zwp = (u64)(uint32_t)pz | (u64)(uint32_t)pw << 32;
+            c[0] = zwp == q32 && v[k].x == p1;
+            c[1] = xy == q21 && pw == p3;
+            c[2] = xy == q32 && v[k].z == p1;
+            c[3] = zw == q21 && v[k].y == p3;
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i)

@@ -209,6 +209,50 @@ def test_short_best_match_inside_interior_tiles(short, n_min):
         assert_parity(w, got, f"tile={tile}")
 
 
+def _lane_boundary_ends(tile: int, L: int, delta: int):
+    """End positions at every lane-0 chunk start (offsets 0..3) of every
+    wavefront, in the first, an interior and the last tile, plus the last
+    positions of each tile (the chunk after the last wavefront's span) and
+    the first of the next. A wavefront of a `tile`-token tile covers
+    min(tile, 1,024) positions, lane 0's chunks start every 256 positions
+    of it, and a row misaligned by `delta` tokens shifts every chunk start
+    back by delta."""
+    ends = set()
+    span = min(tile, 1024)
+    for t0 in (0, tile, 3 * tile):
+        for w in range(tile // span):
+            for k in range(span // 256):
+                for i in range(4):
+                    ends.add(t0 - delta + w * span + 256 * k + i)
+        for i in range(-4, 4):
+            ends.add(t0 + tile + i)
+    return sorted(e for e in ends if 2 <= e <= L - 5)
+
+
+@pytest.mark.parametrize("tile", [1024, 2048, 4096])
+@pytest.mark.parametrize("delta", [0, 1, 2, 3])
+def test_three_token_match_at_every_lane_boundary(tile, delta):
+    """The 3-token register test takes the two tokens before lane 0's chunk
+    from lane 63 of the previous chunk (or from the halo), across the DPP
+    shift. Each request has distinct tokens and one copy of its last three
+    tokens, whose last token sits on one of those boundary positions; the
+    oracle's answer is that copy (match length 3, start e - 2)."""
+    L = 3 * tile + 101
+    rng = np.random.default_rng([47, tile, delta])
+    ends = _lane_boundary_ends(tile, L, delta)
+    hs = []
+    for e in ends:
+        h = rng.permutation(20 * L)[:L].astype(np.int32)
+        h[e - 2:e + 1] = h[L - 3:]
+        hs.append(h)
+    w = wl.Workload("lane_boundary", hs, 3, 12, 8)
+    od, ol, om, oj = oracle.draft(hs, 3, 12, 8)
+    assert om.tolist() == [3] * len(ends) and oj.tolist() == [e - 2 for e in ends]
+    st, got = run_gpu(w, tile=tile, offsets=[delta] * len(hs))
+    assert st == B.PLD_OK
+    assert_parity(w, got, f"tile={tile} delta={delta}")
+
+
 def test_periodic_tails_all_periods():
     hs = []
     rng = np.random.default_rng(17)
