@@ -24,13 +24,18 @@ enum : uint32_t {
     kErrControlInput = 128u   // pld_control: an outcome or lookup input out of range
 };
 
-// Per-request reduction state: the packed key maximum and the arrival
-// counter of the fused gather. One slot per 256 bytes, so that atomics of
-// different requests fall on different cache lines. Zero between calls.
+// Per-request reduction state of the fused gather: the packed key maximum
+// and an accumulator whose low 24 bits count the workgroups that arrived
+// and whose upper 40 bits sum the increases of `key` their atomicMax made
+// (a key is below 2^39: length <= 64 << 32 | end < 2^31; a request has fewer
+// than 2^24 tiles: max_len < 2^31 over tiles of at least 256). The
+// increases telescope, so the sum is the maximum itself. One slot per 256
+// bytes, so that atomics of different requests fall on different cache
+// lines. Zero between calls.
 struct alignas(256) ReqSlot {
     unsigned long long key;
-    unsigned int arrivals;
-    unsigned int pad[61];
+    unsigned long long acc;
+    unsigned int pad[60];
 };
 
 // Draft fusion and long-block scheduling (pld_fuse): parameters as in

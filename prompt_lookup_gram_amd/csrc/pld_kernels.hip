@@ -36,10 +36,11 @@
 //      a 64-bit atomicMax into the request's slot per wavefront (separate
 //      gather kernel), or a workgroup max (LDS atomic) and the fused gather.
 //   5. Fused gather: each workgroup of a multi-tile request merges its max
-//      with a 64-bit atomicMax and counts itself in with an atomic add; the
-//      last one to arrive takes the maximum with an atomic exchange (which
-//      also clears the slot for the next call), writes the draft row and
-//      clears the counter. Single-tile requests emit directly.
+//      with a 64-bit atomicMax and counts itself in with an atomic add that
+//      also carries the increase its atomicMax made; the increases sum to
+//      the maximum, so the last one to arrive has it from its own add. It
+//      writes the draft row and clears the slot for the next call.
+//      Single-tile requests emit directly.
 // pld_gather is the same step 5 as its own kernel, for the unfused mode.
 
 #include <hip/hip_runtime.h>
@@ -505,13 +506,6 @@ __device__ __forceinline__ int4 patch_chunk_append(int4 v, int64_t p0, const Req
     return v;
 }
 
-// Wait until every memory operation this wave issued has completed (for an
-// atomic: has been performed), before issuing the next one.
-__device__ __forceinline__ void wait_vm()
-{
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0), expcnt/lgkmcnt unconstrained
-}
-
 // Scans this wavefront's share of one tile and returns the lane's best key.
 //
 // A workgroup's tile of TILE candidate end positions [t0, t0 + TILE) is cut
@@ -852,8 +846,7 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
 
     __shared__ int4 win[kWaves * kWinW];
     __shared__ int32_t pat[kWaves * kWave];
-    __shared__ u64 wg_best;
-    __shared__ int s_last;
+    __shared__ u64 wbest[kWaves];
 
     const int tid = threadIdx.x;
     // grid: x = request, y = tile (and z, when a request has more tiles than
@@ -962,7 +955,8 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
 
     // 5. wavefront maximum by DPP (only in wavefronts that found a match),
     // then lane 0 merges it: into the request's slot (separate gather
-    // kernel) or into the workgroup's LDS slot (fused gather).
+    // kernel) or, fused, into the workgroup's maximum (one LDS word per
+    // wavefront and a single barrier, after which wavefront 0 alone goes on).
     const bool found = __any(best != 0);
     if (found)
         best = wave_max_u64(best);
@@ -973,47 +967,66 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
             __hip_atomic_fetch_max(&a.slots[b].key, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    if (tid == 0)
-        wg_best = 0;
-    __syncthreads();
-    if (found && leader)
-        __hip_atomic_fetch_max(&wg_best, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // the workgroup's maximum: one LDS word per wavefront, one barrier;
+    // then wavefront 0 alone merges, and emits if it is the last to arrive
+    u64 m = best;
+    if constexpr (kWaves > 1) {
+        if (leader)
+            wbest[tid / kWave] = found ? best : 0ull;
+        __syncthreads();
+        if (tid >= kWave)
+            return;
+        m = wbest[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            m = wbest[w] > m ? wbest[w] : m;
+    } else if (!found) {
+        m = 0;
+    }
 
     // 6. fused gather: the last workgroup of the request to arrive emits the
     // draft. Only atomic read-modify-writes at agent scope cross
     // workgroups: each is performed at the location's single point of
-    // coherence, and each workgroup waits for its max to be performed before
-    // it counts itself in, so the workgroup that counts last reads (and
-    // clears) the final maximum with an atomic exchange.
-    __syncthreads();
-    if (tid == 0) {
-        u64 m = wg_best;
-        int last = 1;
-        if (arrive > 1) {
+    // coherence. A workgroup with a match takes its atomicMax's return
+    // first and adds the increase it made to the maximum together with its
+    // arrival; the increases of all atomicMax calls sum to the final
+    // maximum, so the workgroup that counts last reads it from its own add
+    // (and clears the slot).
+    int last = 1;
+    if (arrive > 1) {
+        if (tid == 0) {
+            // this workgroup's increase of the maximum (0 without a match),
+            // known once its atomicMax returns, is added with its arrival
+            u64 inc = 0;
             if (m) {
-                __hip_atomic_fetch_max(&a.slots[b].key, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                wait_vm();
+                const u64 old = __hip_atomic_fetch_max(&a.slots[b].key, m, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+                inc = m > old ? m - old : 0;
             }
-            const unsigned prev = __hip_atomic_fetch_add(&a.slots[b].arrivals, 1u, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-            last = prev == (unsigned)(arrive - 1);
+            const u64 prev = __hip_atomic_fetch_add(&a.slots[b].acc, (inc << 24) + 1,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = (uint32_t)(prev & 0xffffffu) == (uint32_t)(arrive - 1);
             if (last) {
-                m = __hip_atomic_exchange(&a.slots[b].key, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_exchange(&a.slots[b].arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                // every other workgroup's increase is in `prev`: their maxima
+                // returned before they counted in
+                m = (prev >> 24) + inc;
+                __hip_atomic_store(&a.slots[b].key, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&a.slots[b].acc, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-        wg_best = m;
-        s_last = last;
+        // lane 0's results to the whole wavefront
+        last = __builtin_amdgcn_readfirstlane(last);
+        m = ((u64)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(m >> 32)) << 32) |
+            (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)m);
     }
-    __syncthreads();
-    if (!s_last)
+    if (!last)
         return;
     if constexpr (APPEND) {
-        emit<true>(a, b, r, wg_best, tid, THREADS);
+        emit<true>(a, b, r, m, tid, kWave);
         if (tid == 0 && r.add > 0)
             a.app_lengths[b] = r.L;
     } else {
-        emit_request<FUSE, CONTROL>(a, b, r, wg_best, tid, THREADS, pre, cpre);
+        emit_request<FUSE, CONTROL>(a, b, r, m, tid, kWave, pre, cpre);
     }
 }
 
