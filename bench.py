@@ -830,6 +830,8 @@ def bench_stream(args, torch, B, wl, dev):
     else:
         ctx = B.pld_create(nb, max_len, own_store=True)
     rows, lens = B.pld_histories(ctx)
+    if not (args.index or args.ngram):
+        B.pld_configure(ctx, args.tile, args.fused)
     tile = None if (args.index or args.ngram) else B.pld_scan_tile(ctx, nb)
     # controller inputs: every outcome "0 accepted in time 1.0" is valid for
     # any previous choice, so the captured steps need no host round trip
@@ -988,7 +990,8 @@ def bench_stream(args, torch, B, wl, dev):
         rec["steps_requested"], rec["warmup_requested"] = args.steps, args.warmup
     if not (args.index or args.ngram):
         one_launch = args.append_draft and not (args.control and not args.control_fused)
-        plain = not args.control and start_len == wl.STREAM_START_LEN
+        plain = (not args.control and start_len == wl.STREAM_START_LEN
+                 and args.tile in (0, tile) and args.fused in (-1, 1))
         prof = (PROFILE_APPEND_DRAFT if one_launch else PROFILE_STREAM) if plain else None
         kernels = (["pld_scan"] + ([] if args.append_draft else ["pld_append_kernel"])
                    + (["pld_control_kernel"] if args.control and not args.control_fused else []))
