@@ -230,3 +230,45 @@ def test_sync_sees_errors_from_other_streams():
         assert B.pld_sync(ctx, s1) == B.PLD_OK
     finally:
         B.pld_destroy(ctx)
+
+
+def _every_tile_matches(batch: int, L: int, tile: int, seed: int):
+    """Histories of distinct tokens in which every tile (but the last two)
+    holds one copy of the history's last l tokens, l drawn from 4..12 per
+    tile, ending at a random position inside the tile: every workgroup of
+    the request has its own maximum, and the request's key is raised
+    many times, in whatever order the workgroups reach the merge."""
+    rng = np.random.default_rng([61, seed])
+    hs = []
+    for _ in range(batch):
+        h = rng.permutation(20 * L)[:L].astype(np.int32)
+        suffix = h[L - 12:].copy()
+        for t in range((L - 1) // tile - 1):
+            ell = int(rng.integers(4, 13))
+            e = t * tile + int(rng.integers(ell + 1, tile - 1))
+            h[e - ell + 1:e + 1] = suffix[12 - ell:]
+        hs.append(h)
+    return wl.Workload(f"every_tile_{seed}", hs, 4, 12, 16)
+
+
+@pytest.mark.parametrize("tile", [256, 1024, 4096])
+def test_repeat_every_tile_raises_the_maximum(tile):
+    """Every workgroup of a request has a match (up to 255 per request at
+    256-token tiles), 20 calls back to back, each checked against the
+    oracle: the merge's key increases must add up to the maximum in every
+    order the workgroups arrive in."""
+    w = _every_tile_matches(8, 65_536, tile, tile)
+    od, ol, om, oj = oracle.draft(w.histories, w.n_min, w.n_max, w.k_max)
+    assert (om >= 4).all()
+    db = B.DeviceBatch(w.histories)
+    ctx = B.pld_create(w.batch, db.max_len)
+    try:
+        B.pld_configure(ctx, tile, 1)
+        outs = _outs(20, w.batch, w.k_max)
+        for i in range(20):
+            B.pld_draft_batch_pos(ctx, db.rows, db.lengths, w.batch, w.n_min, w.n_max,
+                                  w.k_max, outs[0][i], outs[1][i], outs[2][i], outs[3][i])
+        assert B.pld_sync(ctx) == B.PLD_OK
+    finally:
+        B.pld_destroy(ctx)
+    _first_mismatch(w, outs, f"every tile matching, tile {tile}")
