@@ -22,19 +22,27 @@
 // wavefront takes a contiguous share of the tile and works on its own):
 //   1. Coalesced, non-temporal 16-byte loads bring the wavefront's span plus
 //      the 64 tokens to its left into registers; rows that are not 16-byte
-//      aligned are read as aligned chunks shifted by the misalignment.
+//      aligned are read as aligned chunks shifted by the misalignment. A
+//      request's last tile (unless it is also its first) loads through a
+//      buffer resource whose record count ends at the row's last 16-byte
+//      block, so the blocks past the row read as zeros with no branch, and
+//      it runs the interior tiles' tests; its first tile range-checks every
+//      chunk and position.
 //   2. The registers are staged in the wavefront's own LDS region.
 //   3. Rejection in registers: a position survives only if it holds the
 //      history's last token (about 2-4% on Zipf text) and, when n_min >= 3,
 //      its two predecessors hold the two tokens before that (the tokens
 //      before a chunk come from the neighbouring lane by a DPP wavefront
 //      shift; two of the three tokens are compared as one 64-bit pair);
-//      survivors extend backwards from LDS up to m tokens, several tokens
-//      per LDS round trip.
+//      survivors extend backwards from LDS up to m tokens: when a wavefront
+//      has only a few, the whole wavefront extends each in one LDS round
+//      trip (one token per lane, the first mismatch from a ballot);
+//      otherwise each lane extends its own, several tokens per round trip.
 //   4. Per-thread max -> wavefront max (DPP row shifts and broadcasts on
 //      2x32-bit halves), only in wavefronts that found a match, then either
 //      a 64-bit atomicMax into the request's slot per wavefront (separate
-//      gather kernel), or a workgroup max (LDS atomic) and the fused gather.
+//      gather kernel), or a workgroup max (one LDS word per wavefront and a
+//      single barrier) and the fused gather.
 //   5. Fused gather: each workgroup of a multi-tile request merges its max
 //      with a 64-bit atomicMax and counts itself in with an atomic add that
 //      also carries the increase its atomicMax made; the increases sum to
@@ -47,7 +55,6 @@
 #include <stdint.h>
 
 #include <mutex>
-#include <type_traits>
 
 #include "pld_control_step.h"
 #include "pld_kernels.h"
@@ -60,6 +67,7 @@ constexpr int kHalo = 64;                 // >= PLD_N_MAX_LIMIT - 1, multiple of
 constexpr int kHaloChunks = kHalo / 4;    // 16-byte chunks of halo
 constexpr int kWave = 64;
 constexpr int kExtBlock = 4;             // tokens compared per LDS round trip when extending
+constexpr int kWaveExt = 4;              // most survivors a wavefront extends together
 constexpr unsigned kGridY = 65535;       // largest y extent of a grid
 
 typedef unsigned long long u64;
@@ -556,6 +564,54 @@ __device__ __forceinline__ void load_interior(const int4 *arow, int64_t t0, bool
         v[k] = gld_stream(real ? arow + (gq0 + kHaloChunks + k * kWave + lane) : zero16);
 }
 
+// Buffer resource over one wavefront's window of a tile (load_window).
+// Word 3 of the resource: 32-bit data format, no swizzle, no thread-id
+// offset (the CDNA raw-buffer layout).
+constexpr int32_t kBufWord3 = 0x00020000;
+
+__device__ __forceinline__ int4 bld_stream(__amdgpu_buffer_rsrc_t rs, int32_t off)
+{
+    const v4i32 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2 /* nt */);
+    return make_int4(x[0], x[1], x[2], x[3]);
+}
+
+// Issues this lane's loads of a request's last tile, one that starts at
+// least kHalo + 4 tokens into its row, through a buffer resource over this
+// wavefront's window. The window's 16-byte blocks begin at local token 0 (a
+// 16-byte boundary of the row); (avail + 3) / 4 of them hold a token of the
+// row, avail being the row's length less local token 0's position. The
+// resource's record count ends there, so the hardware returns zeros for
+// every later block without touching memory: the chunks past the row cost
+// no branch and no address select. The block that holds the row's last
+// token is read whole (an aligned 16-byte block lies on one page); its
+// positions past the end are never candidates. Chunk offsets are multiples
+// of 16 and so is the record count, so every block is either wholly in
+// range or wholly out.
+template <int TILE, int THREADS>
+__device__ __forceinline__ void load_window(const int4 *wbase, int32_t avail,
+                                            int4 (&v)[WaveGeom<TILE, THREADS>::kPer + 1])
+{
+    constexpr int kSpan = WaveGeom<TILE, THREADS>::kSpan;
+    constexpr int kPer = WaveGeom<TILE, THREADS>::kPer;
+    constexpr int kWinW = kHaloChunks + kSpan + 1;
+    const int lane = threadIdx.x & (kWave - 1);
+    // the window's base and size are the same in every lane: taken into
+    // scalar registers, so the resource needs no per-lane loop
+    const int32_t av = __builtin_amdgcn_readfirstlane(avail < 4 * kWinW ? avail : 4 * kWinW);
+    const int32_t nb = av <= 0 ? 0 : (av + 3) >> 2;
+    const uint64_t wb = (uint64_t)(uintptr_t)wbase;
+    const uint64_t wbu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)wb) |
+                         (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(wb >> 32)) << 32;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)wbu, (short)0, nb * 16, kBufWord3);
+    // the extra chunk first: slot 0's tests need the halo
+    const int qx = lane < kHaloChunks ? lane : (lane == kHaloChunks ? kHaloChunks + kSpan : kHaloChunks + lane);
+    v[kPer] = bld_stream(rs, 16 * qx);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        v[k] = bld_stream(rs, 16 * (kHaloChunks + lane) + 16 * kWave * k);
+}
+
 // Issues this lane's loads of any tile of a strided row whose length is
 // `bound`, before the length is read: the chunks that lie inside [0, bound)
 // are loaded whole, the others read the row's first chunk in their place
@@ -588,7 +644,8 @@ struct SufPre {
     int32_t p1, p2, p3, pv;
 };
 
-template <int TILE, int THREADS, bool CHECKED, bool FILTER3, bool PRELOADED, bool APPEND>
+template <int TILE, int THREADS, bool CHECKED, bool FILTER3, bool PRELOADED, bool APPEND,
+          bool TAIL = false>
 __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64_t t0,
                                          int32_t mhat, int4 *lds_win, int32_t *lds_pat,
                                          int4 (&v)[WaveGeom<TILE, THREADS>::kPer + 1],
@@ -651,6 +708,11 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
         }
     } else if constexpr (PRELOADED) {
         // the caller issued this tile's loads before the length was known
+    } else if constexpr (TAIL) {
+        // the row's length less the position of local token 0: the true
+        // difference lies in (-TILE - kHalo, 2^31), so it is exact modulo 2^32
+        const int32_t avail = (int32_t)((uint32_t)r.L - (uint32_t)pq0);
+        load_window<TILE, THREADS>(arow + gq0, avail, v);
     } else if constexpr (!CHECKED) {
         load_interior<TILE, THREADS>(arow, t0, true, a.zero16, v);
     } else {
@@ -685,8 +747,8 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
 
     // 3. rejection tests. Bit 4k + i of `bits` says token i of slot k (slot
     // kPer: the extra chunk) goes on to extend.
-    static_assert(4 * (kPer + 1) <= 64, "survivor bitmask is 64 bits");
-    typedef typename std::conditional<4 * (kPer + 1) <= 32, uint32_t, u64>::type mask_t;
+    static_assert(4 * (kPer + 1) <= 32, "survivor bitmask is 32 bits");
+    typedef uint32_t mask_t;
     mask_t bits = 0;
     // Positions owned by this wavefront: rel in [lo, hi). The span's
     // positions belong to it, the chunk after the span only to the last
@@ -746,14 +808,60 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
     }
 
     // 4. survivors extend backwards from LDS. Most wavefronts have none and
-    // skip this with one branch; otherwise each lane walks its bitmask.
+    // skip this with one branch. With a few survivors (at most kWaveExt
+    // lanes holding one each, the usual case) the whole wavefront extends
+    // each in one LDS round trip: lane j compares the token j before the
+    // candidate's end with suffix token j, and the first mismatch (or
+    // j = lim) is the match length. Otherwise each lane walks its own
+    // bitmask, kExtBlock tokens per round trip.
     u64 best = 0;
     if (__any(bits != 0)) {
+        if constexpr (TAIL) {
+            // a last tile's span runs past its candidates (the suffix itself,
+            // zero blocks and bytes past the row can pass the test there):
+            // keep the positions below hi. The extra chunk was range-checked
+            // when it was tested.
+            mask_t keep = (mask_t)0xf << (4 * kPer);
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {
+                const int32_t r0 = rq0 + 4 * (kHaloChunks + k * kWave + lane);
+                const int32_t n = hi - r0 < 0 ? 0 : (hi - r0 > 4 ? 4 : hi - r0);
+                keep |= (mask_t)((1u << n) - 1u) << (4 * k);
+            }
+            bits &= keep;
+        }
         const int32_t *wt = (const int32_t *)win;
         // lowest rel an extension may reach: position 0 (first tile) or the halo
         const int32_t floor_rel = t0 < kHalo ? -(int32_t)t0 : -kHalo;
+        const u64 holders = __ballot(bits != 0);
+        if (__popcll(holders) <= kWaveExt && !__any((bits & (bits - 1)) != 0)) {
+            u64 hl = holders;  // the same in every lane, as is wb
+            u64 wb = 0;
+            while (hl) {
+                const int src = __builtin_ctzll(hl);
+                hl &= hl - 1;
+                const uint32_t sb = __builtin_amdgcn_readlane(bits, src);
+                const int bit = __builtin_ctz(sb);
+                const int k = bit >> 2, i = bit & 3;
+                // only the last wavefront's lane kHaloChunks tests the extra chunk
+                const int q = k < kPer ? kHaloChunks + k * kWave + src : kHaloChunks + kSpan;
+                const int32_t slot = 4 * q + i;
+                const int32_t rel = rq0 + slot;
+                const int32_t lim = (!CHECKED || rel - mhat + 1 >= floor_rel) ? mhat : rel - floor_rel + 1;
+                const bool in = lane < lim;
+                const int32_t tk = in ? wt[slot - lane] : 0;
+                const int32_t pt = in ? pat[mhat - 1 - lane] : 0;
+                const u64 miss = __ballot(!in || tk != pt);
+                const int32_t ell = miss ? __builtin_ctzll(miss) : kWave;
+                if (ell >= a.n_min) {
+                    const u64 key = ((u64)(uint32_t)ell << 32) | (uint32_t)(t0 + rel);
+                    wb = key > wb ? key : wb;
+                }
+            }
+            return wb;
+        }
         while (bits) {
-            const int bit = sizeof(mask_t) == 4 ? __builtin_ctz((uint32_t)bits) : __builtin_ctzll((u64)bits);
+            const int bit = __builtin_ctz(bits);
             bits &= bits - 1;
             const int k = bit >> 2, i = bit & 3;
             const int q = k < kPer ? kHaloChunks + k * kWave + lane : qx;
@@ -922,6 +1030,10 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
         // the old length with APPEND) and every position of the tile is a
         // candidate
         const bool interior = t0 >= kHalo + 4 && t0 + TILE + 4 <= (int64_t)(APPEND ? r.split : r.L) - 1;
+        // a request's last tile that is not also its first runs the interior
+        // tests: its window's blocks past the row load as zeros, and its
+        // positions past the candidates are dropped from the survivors
+        const bool tail = !APPEND && !interior && t0 >= kHalo + 4;
         const bool f3 = a.n_min >= 3;
         if (PINNED && !interior)
             best = f3 ? scan_wave<TILE, THREADS, true, true, true, false>(a, r, t0, mhat, win, pat, v, sp)
@@ -932,6 +1044,9 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
         else if (interior)
             best = f3 ? scan_wave<TILE, THREADS, false, true, false, APPEND>(a, r, t0, mhat, win, pat, v, sp)
                       : scan_wave<TILE, THREADS, false, false, false, APPEND>(a, r, t0, mhat, win, pat, v, sp);
+        else if (tail)
+            best = f3 ? scan_wave<TILE, THREADS, false, true, false, false, true>(a, r, t0, mhat, win, pat, v, sp)
+                      : scan_wave<TILE, THREADS, false, false, false, false, true>(a, r, t0, mhat, win, pat, v, sp);
         else
             best = f3 ? scan_wave<TILE, THREADS, true, true, false, APPEND>(a, r, t0, mhat, win, pat, v, sp)
                       : scan_wave<TILE, THREADS, true, false, false, APPEND>(a, r, t0, mhat, win, pat, v, sp);

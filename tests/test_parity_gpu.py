@@ -253,6 +253,39 @@ def test_three_token_match_at_every_lane_boundary(tile, delta):
     assert_parity(w, got, f"tile={tile} delta={delta}")
 
 
+@pytest.mark.parametrize("tile", [1024, 4096])
+@pytest.mark.parametrize("n_min", [1, 3, 4])
+def test_last_tile_past_the_row_end(tile, n_min):
+    """A request's last tile (when it is not also its first) reads its chunks
+    through the row's end: the chunk holding the last token whole, the ones
+    after it from the zero block. Every history here ends in twelve zeros
+    (one earlier run of five zeros sits among nonzero tokens), so the zero
+    chunks, the suffix's own position and any zero bytes past the row pass
+    the register tests; the answer is the 11-token match that ends one token
+    before the row's end, and a position at or past the end would give a
+    longer one. The last tile holds 1..tile+6 candidates (the tile before it
+    is then interior or a last-tile case too), over all four row alignments."""
+    rng = np.random.default_rng([53, tile, n_min])
+    counts = sorted({1, 2, 3, 4, 5, 6, 7, 8, 61, 62, 63, 64, 65, 66, 67, 68, 255, 256, 257}
+                    | {tile + d for d in range(-6, 7)})
+    hs = []
+    for c in counts:
+        L = tile + 1 + c  # tile 1 holds c candidates (positions tile .. L - 2)
+        h = rng.integers(1, 50, L).astype(np.int32)
+        h[-12:] = 0
+        s = int(rng.integers(5, tile - 10))
+        h[s:s + 5] = 0
+        hs.append(h)
+    for n_max in (12, 64):
+        w = wl.Workload("last_tile", hs, n_min, n_max, 16)
+        od, ol, om, oj = oracle.draft(hs, n_min, n_max, 16)
+        assert om.tolist() == [11] * len(hs) and oj.tolist() == [len(h) - 12 for h in hs]
+        for delta in range(4):
+            st, got = run_gpu(w, tile=tile, offsets=[delta] * len(hs))
+            assert st == B.PLD_OK
+            assert_parity(w, got, f"tile={tile} n={n_min}..{n_max} delta={delta}")
+
+
 def test_periodic_tails_all_periods():
     hs = []
     rng = np.random.default_rng(17)
