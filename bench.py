@@ -57,10 +57,12 @@ PROFILES = {1: "pld_scan_c1_b1x4096.md", 2: "pld_scan_c2_b8x25000.md",
 PROFILES_FUSE = {4: "pld_scan_fused_c4_b16x262144.md"}
 PROFILE_APPEND_DRAFT = "pld_scan_append_c5_stream_b64.md"
 PROFILE_STREAM = "pld_scan_c5_stream_b64.md"
-# the sources a counter summary is valid for: the kernels and the C-ABI layer
-# that picks their launch (tile, grid)
+# the sources a counter summary is valid for: the kernels, the C-ABI layer
+# that picks their launch (tile, grid) and the build script that sets their
+# compiler flags
 CSRC = os.path.join(ROOT, "prompt_lookup_gram_amd", "csrc")
-PROFILED_SOURCES = ("pld_kernels.hip", "pld_kernels.h", "pld_device.h", "pld_api.cpp")
+PROFILED_SOURCES = ("pld_kernels.hip", "pld_kernels.h", "pld_device.h", "pld_api.cpp",
+                    os.path.join(os.pardir, "build.py"))
 TIME_SOURCE = ("value, ms_per_step: host clock around the K timed steps, with a device "
                "synchronize on each side; graph_us_per_step, scan_GBps and roofline: HIP "
                "events recorded on the launch stream around the same K steps")

@@ -27,6 +27,12 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
              "-I", INCLUDE, "-I", CSRC]
 
 
+# The scan's atomics are issued by one lane (a workgroup's merge, a
+# wavefront's error bit): the compiler's atomic optimizer would wrap each in a
+# wavefront-wide scan loop that only lengthens the merge on the critical path.
+SOURCE_FLAGS = {"pld_kernels.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+
+
 def sources():
     return [os.path.join(CSRC, "pld_kernels.hip"), os.path.join(CSRC, "pld_index.hip"),
             os.path.join(CSRC, "pld_control.hip"), os.path.join(CSRC, "pld_ngram.hip"),
@@ -39,7 +45,8 @@ def build(verbose: bool = False) -> str:
     for src in sources():
         obj = os.path.join(CSRC, os.path.basename(src) + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC, *HIP_FLAGS, *lang, "-c", src, "-o", obj]
+        cmd = [HIPCC, *HIP_FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), *lang,
+               "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
