@@ -39,16 +39,18 @@
 //      trip (one token per lane, the first mismatch from a ballot);
 //      otherwise each lane extends its own, several tokens per round trip.
 //   4. Per-thread max -> wavefront max (DPP row shifts and broadcasts on
-//      2x32-bit halves), only in wavefronts that found a match, then either
-//      a 64-bit atomicMax into the request's slot per wavefront (separate
-//      gather kernel), or a workgroup max (one LDS word per wavefront and a
-//      single barrier) and the fused gather.
-//   5. Fused gather: each workgroup of a multi-tile request merges its max
-//      with a 64-bit atomicMax and counts itself in with an atomic add that
-//      also carries the increase its atomicMax made; the increases sum to
-//      the maximum, so the last one to arrive has it from its own add. It
-//      writes the draft row and clears the slot for the next call.
-//      Single-tile requests emit directly.
+//      2x32-bit halves) where the lanes hold different values (a value all
+//      lanes share, as the wavefront-level extension leaves, needs none),
+//      then either a 64-bit atomicMax into the request's slot per wavefront
+//      (separate gather kernel), or the fused gather.
+//   5. Fused gather: in a multi-tile request each wavefront with a match
+//      merges its max with a 64-bit atomicMax as soon as its tests end; the
+//      workgroup (one LDS word per wavefront, a single barrier) counts
+//      itself in with an atomic add that also carries the increases its
+//      wavefronts' atomicMax calls made; the increases sum to the maximum,
+//      so the last workgroup to arrive has it from its own add. It writes
+//      the draft row and clears the slot for the next call. Single-tile
+//      requests take the workgroup max and emit directly.
 // pld_gather is the same step 5 as its own kernel, for the unfused mode.
 
 #include <hip/hip_runtime.h>
@@ -1068,13 +1070,21 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
         }
     }
 
-    // 5. wavefront maximum by DPP (only in wavefronts that found a match),
+    // 5. wavefront maximum by DPP (only where the lanes hold different values),
     // then lane 0 merges it: into the request's slot (separate gather
     // kernel) or, fused, into the workgroup's maximum (one LDS word per
     // wavefront and a single barrier, after which wavefront 0 alone goes on).
-    const bool found = __any(best != 0);
-    if (found)
-        best = wave_max_u64(best);
+    {
+        // a value every lane already holds (no match, or the wavefront-level
+        // extension's result) needs no reduction
+        const u64 first = ((u64)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(best >> 32)) << 32) |
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)best);
+        if (__any(best != first))
+            best = wave_max_u64(best);
+        else
+            best = first;
+    }
+    const bool found = best != 0;
     const bool leader = (tid & (kWave - 1)) == 0;
     if (!a.fused) {
         // the gather kernel reads the request's slot after this kernel ends
@@ -1082,19 +1092,36 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
             __hip_atomic_fetch_max(&a.slots[b].key, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    // the workgroup's maximum: one LDS word per wavefront, one barrier;
-    // then wavefront 0 alone merges, and emits if it is the last to arrive
+    // one LDS word per wavefront, one barrier; then wavefront 0 alone
+    // merges, and emits if it is the last to arrive
     u64 m = best;
+    bool premerged = false;  // m is the workgroup's increase of the request's key
     if constexpr (kWaves > 1) {
+        // With several workgroups per request, a wavefront with a match takes
+        // its atomicMax as soon as its own tests end, and leaves the increase
+        // it made; the workgroup adds the sum with its arrival.
+        u64 word = found ? best : 0ull;
+        if (arrive > 1 && found && leader) {
+            const u64 old = __hip_atomic_fetch_max(&a.slots[b].key, best, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+            word = best > old ? best - old : 0ull;
+        }
         if (leader)
-            wbest[tid / kWave] = found ? best : 0ull;
+            wbest[tid / kWave] = word;
         __syncthreads();
         if (tid >= kWave)
             return;
         m = wbest[0];
+        if (arrive > 1) {
+            premerged = true;
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w)
-            m = wbest[w] > m ? wbest[w] : m;
+            for (int w = 1; w < kWaves; ++w)
+                m += wbest[w];
+        } else {
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w)
+                m = wbest[w] > m ? wbest[w] : m;
+        }
     } else if (!found) {
         m = 0;
     }
@@ -1102,11 +1129,11 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
     // 6. fused gather: the last workgroup of the request to arrive emits the
     // draft. Only atomic read-modify-writes at agent scope cross
     // workgroups: each is performed at the location's single point of
-    // coherence. A workgroup with a match takes its atomicMax's return
-    // first and adds the increase it made to the maximum together with its
-    // arrival; the increases of all atomicMax calls sum to the final
-    // maximum, so the workgroup that counts last reads it from its own add
-    // (and clears the slot).
+    // coherence. A wavefront with a match takes its atomicMax's return
+    // before the barrier, and its workgroup adds the increases made to the
+    // maximum together with its arrival; the increases of all atomicMax
+    // calls sum to the final maximum, so the workgroup that counts last
+    // reads it from its own add (and clears the slot).
     // the controller's per-request inputs, issued before the arrival add so
     // that they land within its round trip
     CtlPre cpre{};
@@ -1116,9 +1143,9 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
     if (arrive > 1) {
         if (tid == 0) {
             // this workgroup's increase of the maximum (0 without a match),
-            // known once its atomicMax returns, is added with its arrival
-            u64 inc = 0;
-            if (m) {
+            // known once its atomicMax calls return, is added with its arrival
+            u64 inc = premerged ? m : 0ull;
+            if (!premerged && m) {
                 const u64 old = __hip_atomic_fetch_max(&a.slots[b].key, m, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT);
                 inc = m > old ? m - old : 0;
