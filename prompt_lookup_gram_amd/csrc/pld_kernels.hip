@@ -211,33 +211,6 @@ __device__ __forceinline__ Req load_req(const DraftArgs &a, int b, int tile_toke
     return r;
 }
 
-// A strided row whose length the bounds pin to min_len (min_len equals the
-// stride or max_len, so any other stored length is an error): its fields
-// from min_len alone, with no memory read. The stored length is checked
-// with strided_len_error before the row's results leave the workgroup.
-__device__ __forceinline__ Req pinned_req(const DraftArgs &a, int b, int tile_tokens)
-{
-    Req r;
-    r.h = a.base + (int64_t)b * a.stride;
-    r.src = r.h;
-    r.L = a.min_len;
-    r.split = r.L;
-    r.add = 0;
-    r.app_err = 0;
-    r.err = 0;
-    r.ncand = r.L > 0 ? r.L - 1 : 0;
-    r.ntiles = r.ncand > 0 ? (int32_t)((r.ncand + (int64_t)tile_tokens - 1) / tile_tokens) : 1;
-    return r;
-}
-
-// A scalar (uniform) load through the scalar cache, for history data that
-// no kernel writes while this one runs.
-__device__ __forceinline__ int32_t sld(const int32_t *p)
-{
-    typedef __attribute__((address_space(4))) const int32_t cI;
-    return *(const cI *)p;
-}
-
 // Token p of request r's history: from its row, or with APPEND from the
 // source of this launch's append when p is at or past the old length (one
 // load either way).
@@ -614,44 +587,11 @@ __device__ __forceinline__ void load_window(const int4 *wbase, int32_t avail,
         v[k] = bld_stream(rs, 16 * (kHaloChunks + lane) + 16 * kWave * k);
 }
 
-// Issues this lane's loads of any tile of a strided row whose length is
-// `bound`, before the length is read: the chunks that lie inside [0, bound)
-// are loaded whole, the others read the row's first chunk in their place
-// (scan_wave patches the partial ones once it knows the length, exactly as
-// the checked path loads them).
-template <int TILE, int THREADS>
-__device__ __forceinline__ void load_bounded(const int4 *arow, int64_t t0, int32_t bound,
-                                             int4 (&v)[WaveGeom<TILE, THREADS>::kPer + 1])
-{
-    constexpr int kSpan = WaveGeom<TILE, THREADS>::kSpan;
-    constexpr int kPer = WaveGeom<TILE, THREADS>::kPer;
-    const int wave = threadIdx.x / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t gq0 = (t0 - kHalo) / 4 + (int64_t)wave * kSpan;  // exact
-    const int64_t pq0 = t0 - kHalo + 4 * (int64_t)wave * kSpan;  // rows are 16-byte aligned
-    const int qx = lane < kHaloChunks ? lane : (lane == kHaloChunks ? kHaloChunks + kSpan : -1);
-    const bool inx = qx >= 0 && chunk_inside(pq0 + 4 * qx, bound);
-    v[kPer] = gld_stream(inx ? arow + (gq0 + qx) : arow);
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const int q = kHaloChunks + k * kWave + lane;
-        v[k] = gld_stream(chunk_inside(pq0 + 4 * q, bound) ? arow + (gq0 + q) : arow);
-    }
-}
-
-// The suffix's last three tokens and lane l's token l of it, when they were
-// read before the length (`on`); otherwise scan_wave reads them.
-struct SufPre {
-    bool on;
-    int32_t p1, p2, p3, pv;
-};
-
 template <int TILE, int THREADS, bool CHECKED, bool FILTER3, bool PRELOADED, bool APPEND,
           bool TAIL = false>
 __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64_t t0,
                                          int32_t mhat, int4 *lds_win, int32_t *lds_pat,
-                                         int4 (&v)[WaveGeom<TILE, THREADS>::kPer + 1],
-                                         const SufPre &sp)
+                                         int4 (&v)[WaveGeom<TILE, THREADS>::kPer + 1])
 {
     constexpr int kWaves = THREADS / kWave;
     constexpr int kSpan = TILE / 4 / kWaves;         // chunks per wavefront
@@ -688,27 +628,14 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
         p2 = tok_at<true>(r, r.L - 2);
         p3 = tok_at<true>(r, r.L - (mhat >= 3 ? 3 : 1));
         pv = tok_at<true>(r, r.L - mhat + (lane < mhat ? lane : 0));
-    } else if (sp.on) {
-        p1 = sp.p1;
-        p2 = sp.p2;
-        p3 = sp.p3;
-        pv = sp.pv;
     } else {
         p1 = gld(r.h + r.L - 1);
         p2 = gld(r.h + r.L - 2);
         p3 = gld(r.h + r.L - (mhat >= 3 ? 3 : 1));
         pv = gld(r.h + r.L - mhat + (lane < mhat ? lane : 0));
     }
-    if constexpr (PRELOADED && CHECKED) {
-        // loaded ahead with the row's length as the bound (load_bounded):
-        // only the chunks that straddle an end of the row are left to patch
-#pragma unroll
-        for (int k = 0; k <= kPer; ++k) {
-            const int q = k < kPer ? kHaloChunks + k * kWave + lane : qx;
-            if (q >= 0 && !chunk_inside(pq0 + 4 * q, r.L))
-                v[k] = patch_chunk(v[k], pq0 + 4 * q, r.h, r.L);
-        }
-    } else if constexpr (PRELOADED) {
+    static_assert(!(PRELOADED && CHECKED), "tiles loaded ahead are interior tiles");
+    if constexpr (PRELOADED) {
         // the caller issued this tile's loads before the length was known
     } else if constexpr (TAIL) {
         // the row's length less the position of local token 0: the true
@@ -919,15 +846,7 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
 // new length is stored by the workgroup that emits the draft, and every
 // workgroup of the request (those without candidates too) counts itself in
 // before that, so none of them can read the new length as its old one.
-//
-// PINNED (a strided batch whose bounds pin every length to min_len: min_len
-// equals the stride or max_len): every tile, the first and last included,
-// issues its loads and the suffix's at once, from min_len; the stored length
-// is read alongside and checked before the request's results leave the
-// workgroup (a row that fails the check gets the no-match row and its error
-// bits, as any invalid row does).
-template <int TILE, int THREADS, bool STRIDED, bool FUSE, bool CONTROL, bool APPEND,
-          bool PINNED = false>
+template <int TILE, int THREADS, bool STRIDED, bool FUSE, bool CONTROL, bool APPEND>
 __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int32_t *lengths,
                                                     int32_t batch, int32_t max_len,
                                                     int32_t n_min, int32_t n_max, int64_t stride,
@@ -971,26 +890,9 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
     if (APPEND && tile >= req_tiles)
         return;  // past every request's tiles: counts in nowhere, reads nothing
 
-    static_assert(!PINNED || (STRIDED && !APPEND && !FUSE && !CONTROL), "pinned: plain strided scan");
     int4 v[kPer + 1];
     bool ahead = false;
-    SufPre sp{};
-    int32_t stored_len = 0;
-    if constexpr (PINNED) {
-        // L = min_len >= 2: the suffix first (its three last tokens through
-        // the scalar cache), then the tile, then the stored length
-        const int32_t *hrow = a.base + (int64_t)b * stride;
-        const int lane = tid & (kWave - 1);
-        const int32_t mh = min_len - 1 < n_max ? min_len - 1 : n_max;
-        sp.on = true;
-        sp.pv = gld(hrow + (min_len - mh + (lane < mh ? lane : 0)));
-        sp.p1 = sld(hrow + (min_len - 1));
-        sp.p2 = sld(hrow + (min_len - 2));
-        sp.p3 = sld(hrow + (min_len - (mh >= 3 ? 3 : 1)));
-        ahead = true;
-        load_bounded<TILE, THREADS>((const int4 *)hrow, t0, min_len, v);
-        stored_len = a.lengths[b];
-    } else if constexpr (STRIDED && !APPEND) {
+    if constexpr (STRIDED && !APPEND) {
         // interior for every row of length >= min_len
         ahead = t0 >= kHalo + 4 && t0 + TILE + 4 <= (int64_t)min_len - 1;
         const int4 *arow = (const int4 *)(a.base + (int64_t)b * stride);
@@ -998,7 +900,7 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
         load_interior<TILE, THREADS>(arow, t0, ahead, arow, v);
     }
 
-    const Req r = PINNED ? pinned_req(a, b, TILE) : load_req<APPEND>(a, b, TILE);
+    const Req r = load_req<APPEND>(a, b, TILE);
     // the fusion's per-request inputs, issued with the request's length.
     // (Issued late, before the arrival add, as the controller's are below,
     // they measured slower on a batch of 8 requests of 25,000 tokens.)
@@ -1037,39 +939,19 @@ __global__ __launch_bounds__(THREADS) void pld_scan(const void *rows, const int3
         // positions past the candidates are dropped from the survivors
         const bool tail = !APPEND && !interior && t0 >= kHalo + 4;
         const bool f3 = a.n_min >= 3;
-        if (PINNED && !interior)
-            best = f3 ? scan_wave<TILE, THREADS, true, true, true, false>(a, r, t0, mhat, win, pat, v, sp)
-                      : scan_wave<TILE, THREADS, true, false, true, false>(a, r, t0, mhat, win, pat, v, sp);
-        else if (STRIDED && !APPEND && ahead && r.err == 0)
-            best = f3 ? scan_wave<TILE, THREADS, false, true, true, false>(a, r, t0, mhat, win, pat, v, sp)
-                      : scan_wave<TILE, THREADS, false, false, true, false>(a, r, t0, mhat, win, pat, v, sp);
+        if (STRIDED && !APPEND && ahead && r.err == 0)
+            best = f3 ? scan_wave<TILE, THREADS, false, true, true, false>(a, r, t0, mhat, win, pat, v)
+                      : scan_wave<TILE, THREADS, false, false, true, false>(a, r, t0, mhat, win, pat, v);
         else if (interior)
-            best = f3 ? scan_wave<TILE, THREADS, false, true, false, APPEND>(a, r, t0, mhat, win, pat, v, sp)
-                      : scan_wave<TILE, THREADS, false, false, false, APPEND>(a, r, t0, mhat, win, pat, v, sp);
+            best = f3 ? scan_wave<TILE, THREADS, false, true, false, APPEND>(a, r, t0, mhat, win, pat, v)
+                      : scan_wave<TILE, THREADS, false, false, false, APPEND>(a, r, t0, mhat, win, pat, v);
         else if (tail)
-            best = f3 ? scan_wave<TILE, THREADS, false, true, false, false, true>(a, r, t0, mhat, win, pat, v, sp)
-                      : scan_wave<TILE, THREADS, false, false, false, false, true>(a, r, t0, mhat, win, pat, v, sp);
+            best = f3 ? scan_wave<TILE, THREADS, false, true, false, false, true>(a, r, t0, mhat, win, pat, v)
+                      : scan_wave<TILE, THREADS, false, false, false, false, true>(a, r, t0, mhat, win, pat, v);
         else
-            best = f3 ? scan_wave<TILE, THREADS, true, true, false, APPEND>(a, r, t0, mhat, win, pat, v, sp)
-                      : scan_wave<TILE, THREADS, true, false, false, APPEND>(a, r, t0, mhat, win, pat, v, sp);
+            best = f3 ? scan_wave<TILE, THREADS, true, true, false, APPEND>(a, r, t0, mhat, win, pat, v)
+                      : scan_wave<TILE, THREADS, true, false, false, APPEND>(a, r, t0, mhat, win, pat, v);
     }
-    if constexpr (PINNED) {
-        // the stored length: any value but min_len makes the row invalid. Its
-        // tile 0 reports the error and writes the no-match row alone (as
-        // for any invalid row, whose only tile is tile 0); the other tiles
-        // leave without counting in.
-        const uint32_t lerr = strided_len_error(a, stored_len);
-        if (lerr) {
-            if (tile != 0)
-                return;
-            if (tid == 0)
-                atomicOr(a.err, lerr);
-            if (a.fused)
-                emit<false>(a, b, r, 0ull, tid, THREADS);
-            return;  // unfused: pld_gather finds the same length and writes the row
-        }
-    }
-
     // 5. wavefront maximum by DPP (only where the lanes hold different values),
     // then lane 0 merges it: into the request's slot (separate gather
     // kernel) or, fused, into the workgroup's maximum (one LDS word per
@@ -1262,13 +1144,6 @@ hipError_t launch_scan(const DraftArgs &a, int64_t tiles_per_req, hipStream_t s)
         hipLaunchKernelGGL((pld_scan<TILE, THREADS, true, false, false, true>),
                            grid, dim3(THREADS), 0, s, (const void *)a.base,
                            a.lengths, a.batch, a.max_len, a.n_min, a.n_max, a.stride, 0, a);
-    else if (a.stride && a.min_len >= 2 &&
-             ((int64_t)a.min_len == a.stride || a.min_len == a.max_len))
-        // every valid length is min_len: the pinned scan
-        hipLaunchKernelGGL((pld_scan<TILE, THREADS, true, false, false, false, true>),
-                           grid, dim3(THREADS), 0, s, (const void *)a.base,
-                           a.lengths, a.batch, a.max_len, a.n_min, a.n_max, a.stride, a.min_len,
-                           a);
     else if (a.stride)
         hipLaunchKernelGGL((pld_scan<TILE, THREADS, true, false, false, false>),
                            grid, dim3(THREADS), 0, s, (const void *)a.base,

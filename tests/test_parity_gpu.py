@@ -543,8 +543,8 @@ def pinned_batch(seed, L, batch=6, n_min=4, n_max=12, k_max=16):
 
 
 # a batch whose bounds pin every length (min_len equals the stride or
-# max_len): every tile loads before the length is read, and the stored length
-# is checked afterwards
+# max_len): the strided scan's interior tiles load before the length is read,
+# and every stored length is still checked against the bounds
 @pytest.mark.parametrize("L", [2, 3, 5, 13, 64, 67, 68, 69, 255, 256, 257, 1031, 4096, 4097,
                                4100, 8195])
 @pytest.mark.parametrize("pin", ["stride", "max_len"])

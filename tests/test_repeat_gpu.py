@@ -80,8 +80,8 @@ def test_repeat_default_tile(cfg):
 
 def test_repeat_pinned_strided():
     """Workload 4 as one [16, 262,144] buffer whose stride pins every length:
-    the scan that issues its loads before reading the stored lengths, 100
-    calls back to back."""
+    the strided scan, whose interior tiles issue their loads before reading
+    the stored lengths, 100 calls back to back."""
     w = wl.config4()
     sb = B.StridedBatch(w.histories)
     assert sb.min_len == sb.stride == sb.max_len  # the pinned case
