@@ -233,11 +233,13 @@ def test_sync_sees_errors_from_other_streams():
 
 
 def _every_tile_matches(batch: int, L: int, tile: int, seed: int):
-    """Histories of distinct tokens in which every tile (but the last two)
-    holds one copy of the history's last l tokens, l drawn from 4..12 per
-    tile, ending at a random position inside the tile: every workgroup of
-    the request has its own maximum, and the request's key is raised
-    many times, in whatever order the workgroups reach the merge."""
+    """Histories of distinct tokens in which every span of `tile` positions
+    (but the last two) holds one copy of the history's last l tokens, l
+    drawn from 4..12 per span, ending at a random position inside the span:
+    with the span a tile, every workgroup of the request has its own
+    maximum; with the span a wavefront's share of a tile, every wavefront
+    has. The request's key is raised many times, in whatever order the
+    workgroups and wavefronts reach the merge."""
     rng = np.random.default_rng([61, seed])
     hs = []
     for _ in range(batch):
@@ -272,3 +274,27 @@ def test_repeat_every_tile_raises_the_maximum(tile):
     finally:
         B.pld_destroy(ctx)
     _first_mismatch(w, outs, f"every tile matching, tile {tile}")
+
+
+@pytest.mark.parametrize("tile", [2048, 4096])
+def test_repeat_every_wavefront_raises_the_maximum(tile):
+    """Every wavefront of every workgroup has a match (a copy planted in each
+    1,024-position wavefront span; 2 or 4 wavefronts per workgroup), 20
+    calls back to back, each checked against the oracle: each wavefront's
+    atomicMax increase must reach its workgroup's arrival add, and the
+    increases must add up to the maximum in every order."""
+    w = _every_tile_matches(8, 65_536, 1024, 7 + tile)
+    od, ol, om, oj = oracle.draft(w.histories, w.n_min, w.n_max, w.k_max)
+    assert (om >= 4).all()
+    db = B.DeviceBatch(w.histories)
+    ctx = B.pld_create(w.batch, db.max_len)
+    try:
+        B.pld_configure(ctx, tile, 1)
+        outs = _outs(20, w.batch, w.k_max)
+        for i in range(20):
+            B.pld_draft_batch_pos(ctx, db.rows, db.lengths, w.batch, w.n_min, w.n_max,
+                                  w.k_max, outs[0][i], outs[1][i], outs[2][i], outs[3][i])
+        assert B.pld_sync(ctx) == B.PLD_OK
+    finally:
+        B.pld_destroy(ctx)
+    _first_mismatch(w, outs, f"every wavefront matching, tile {tile}")
