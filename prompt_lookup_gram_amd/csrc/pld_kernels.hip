@@ -240,6 +240,13 @@ __device__ __forceinline__ void emit(const DraftArgs &a, int b, const Req &r,
         const int32_t follow = r.L - 1 - e;
         d = follow < a.k_max ? follow : a.k_max;
     }
+    // the per-request outputs first: they do not wait for the continuation
+    if (tid == 0) {
+        a.out_len[b] = d;
+        a.out_match[b] = m;
+        if (a.out_pos)
+            a.out_pos[b] = key != 0 ? e - m + 1 : -1;
+    }
     int32_t *row = a.out_draft + (int64_t)b * a.k_max;
     const int32_t *src = r.h + (int64_t)e + 1;
     for (int t = tid; t < a.k_max; t += nthreads) {
@@ -247,12 +254,6 @@ __device__ __forceinline__ void emit(const DraftArgs &a, int b, const Req &r,
             row[t] = t < d ? tok_at<true>(r, (int64_t)e + 1 + t) : -1;
         else
             row[t] = t < d ? gld(src + t) : -1;
-    }
-    if (tid == 0) {
-        a.out_len[b] = d;
-        a.out_match[b] = m;
-        if (a.out_pos)
-            a.out_pos[b] = key != 0 ? e - m + 1 : -1;
     }
 }
 
