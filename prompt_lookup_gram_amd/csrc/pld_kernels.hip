@@ -37,7 +37,8 @@
 //      survivors extend backwards from LDS up to m tokens: when a wavefront
 //      has only a few, the whole wavefront extends each in one LDS round
 //      trip (one token per lane, the first mismatch from a ballot);
-//      otherwise each lane extends its own, several tokens per round trip.
+//      otherwise each lane extends its own: 4 tokens in the first round
+//      trip, 8 in each later one.
 //   4. Per-thread max -> wavefront max (DPP row shifts and broadcasts on
 //      2x32-bit halves) where the lanes hold different values (a value all
 //      lanes share, as the wavefront-level extension leaves, needs none),
@@ -68,7 +69,7 @@ namespace {
 constexpr int kHalo = 64;                 // >= PLD_N_MAX_LIMIT - 1, multiple of 4
 constexpr int kHaloChunks = kHalo / 4;    // 16-byte chunks of halo
 constexpr int kWave = 64;
-constexpr int kExtBlock = 4;             // tokens compared per LDS round trip when extending
+constexpr int kExtBlock = 4;             // tokens a lane compares in its first LDS round trip when extending (twice as many later)
 constexpr int kWaveExt = 4;              // most survivors a wavefront extends together
 constexpr unsigned kGridY = 65535;       // largest y extent of a grid
 
@@ -743,7 +744,8 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
     // each in one LDS round trip: lane j compares the token j before the
     // candidate's end with suffix token j, and the first mismatch (or
     // j = lim) is the match length. Otherwise each lane walks its own
-    // bitmask, kExtBlock tokens per round trip.
+    // bitmask, kExtBlock tokens in its first round trip per survivor and
+    // 2 * kExtBlock in each later one.
     u64 best = 0;
     if (__any(bits != 0)) {
         if constexpr (TAIL) {
@@ -799,13 +801,14 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
             const int32_t rel = rq0 + slot;
             int32_t ell = k < kPer ? ell0 : 1;
             ell = ell < mhat ? ell : mhat;
-            // compare up to kExtBlock further tokens per LDS round trip: the
-            // reads are independent, a mismatch mask marks the first token
-            // that differs (or lies past m or before position 0)
+            // each round trip's reads are independent; a mismatch mask marks
+            // the first token that differs (or lies past m or before
+            // position 0)
             const int32_t lim = (!CHECKED || rel - mhat + 1 >= floor_rel) ? mhat : rel - floor_rel + 1;
-            while (ell < lim) {
-                // all reads first (indices clamped into range, no branches),
-                // then the comparisons
+            // the first round trip compares kExtBlock tokens (most survivors
+            // fail there); a candidate that passes it is likely a long match,
+            // and the following rounds compare twice as many
+            if (ell < lim) {
                 int32_t tk[kExtBlock], pt[kExtBlock];
 #pragma unroll
                 for (int u = 0; u < kExtBlock; ++u) {
@@ -819,8 +822,27 @@ __device__ __forceinline__ u64 scan_wave(const DraftArgs &a, const Req &r, int64
                     miss |= (uint32_t)((tk[u] != pt[u]) | (ell + u >= lim)) << u;
                 const int run = __builtin_ctz(miss);
                 ell += run;
-                if (run < kExtBlock)
-                    break;
+                if (run == kExtBlock) {
+                    while (ell < lim) {
+                        // all reads first (indices clamped into range, no
+                        // branches), then the comparisons
+                        int32_t tk2[2 * kExtBlock], pt2[2 * kExtBlock];
+#pragma unroll
+                        for (int u = 0; u < 2 * kExtBlock; ++u) {
+                            const int32_t j = ell + u < lim ? ell + u : ell;
+                            tk2[u] = wt[slot - j];
+                            pt2[u] = pat[mhat - 1 - j];
+                        }
+                        uint32_t miss2 = 1u << (2 * kExtBlock);
+#pragma unroll
+                        for (int u = 0; u < 2 * kExtBlock; ++u)
+                            miss2 |= (uint32_t)((tk2[u] != pt2[u]) | (ell + u >= lim)) << u;
+                        const int run2 = __builtin_ctz(miss2);
+                        ell += run2;
+                        if (run2 < 2 * kExtBlock)
+                            break;
+                    }
+                }
             }
             if (ell >= a.n_min) {
                 const u64 key = ((u64)(uint32_t)ell << 32) | (uint32_t)(t0 + rel);
